@@ -1,0 +1,47 @@
+"""The pins must catch plausible mistakes in the oracle.
+
+Each case copies the oracle's C source, plants one mistake in the copy, builds
+it with gcc in a temporary directory and runs the pin suite against it in a
+subprocess; the suite must fail.  The committed oracle is never modified.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "fp8bs_oracle.c")
+
+MUTANTS = {
+    "dropped_last_chunk": ("for (c = 0; c < K / 128; ++c)", "for (c = 0; c + 1 < K / 128; ++c)"),
+    "lost_sign": ("return s ? -v : v;", "return v;"),
+    "subnormal_scale": ("v = ldexp((double)m, -9);", "v = ldexp((double)m, -10);"),
+    "exponent_bias": ("v = ldexp((double)(8 + m), e - 10);", "v = ldexp((double)(8 + m), e - 9);"),
+    "first_chunk_scale_only": ("s = (double)sa[c * sa_step] * (double)sb[c * sb_step];",
+                               "s = (double)sa[0] * (double)sb[c * sb_step];"),
+    "b_scale_block_index": ("SB + (g * nb + n / 128) * kb", "SB + (g * nb + (n / 128 + 1) % nb) * kb"),
+    "b_row_as_column_block": ("B + (g * N + n) * K", "B + (g * N + (n ^ 1) % N) * K"),
+    "truncating_round": ("r = rint(n);", "r = floor(n);"),
+    "rounds_through_fp32": ("uint16_t sign = signbit(x) ? 0x8000u : 0u;",
+                            "uint16_t sign = signbit(x) ? 0x8000u : 0u; x = (double)(float)x;"),
+    "masked_off_by_one": ("if (r >= valid) continue;", "if (r > valid) continue;"),
+    "padding_written": ("if (g < 0 || g >= G) continue;", "if (g >= G) continue; if (g < 0) g = 0;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not found exactly once"
+    mut_c = tmp_path / "mutant.c"
+    mut_c.write_text(src.replace(old, new))
+    so = tmp_path / "libmutant.so"
+    subprocess.run(["gcc", "-std=c11", "-O2", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared",
+                    "-o", str(so), str(mut_c), "-lm"], check=True)
+    env = dict(os.environ, FP8BS_ORACLE_LIB=str(so))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"pins did not catch mutant {name}:\n{r.stdout[-2000:]}"
