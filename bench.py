@@ -1,0 +1,259 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-scaled FP8 GEMM on one MI355X.
+
+A step is one pass over the workload: every GEMM shape of the chosen family
+run once, back to back, on one stream (default: the dense prefill sweep,
+M = 4096 x six (N, K) shapes).  Inputs are synthetic, seeded, and resident in
+HBM before timing starts.  Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--family F] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "FP8 TFLOP/s and % of MI355X FP8 MFMA peak (HBM GB/s for small M), 1 GPU"
+PEAK_FP8_TFLOPS = 5000.0          # MI355X dense FP8 MFMA, published
+PEAK_HBM_GBS = 8000.0             # MI355X HBM3E, published
+KERNEL_SOURCES = ["moe_grouped_gemm_block_amd/csrc/fp8bs_gemm.hip",
+                  "moe_grouped_gemm_block_amd/csrc/fp8bs_instances.inc"]
+FAMILY_NAMES = {
+    0: "dense M=128 N=2112 K=7168",
+    1: "dense prefill sweep M=4096, (N,K) in {(2112,7168),(24576,1536),(32768,512),"
+       "(7168,16384),(4096,7168),(7168,2048)}",
+    2: "dense decode sweep M in {64,128,256} x (N,K) in {(7168,7168),(7168,2048),(4096,7168)}",
+    3: "MoE contiguous G=8, multinomial rows ~32768, (N,K) in {(4096,7168),(7168,2048)}",
+    4: "MoE masked G=16, max_m=256, masked_m~U{1..256}, (N,K) in {(4096,7168),(7168,2048)}",
+}
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def load_traffic(name: str):
+    """HBM bytes per launch measured with rocprofv3 --pmc (FETCH_SIZE + WRITE_SIZE, scaled
+    by a plain copy kernel) for this kernel source; None when absent or stale."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        data = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if data.get("source_sha256") != kernel_source_hash():
+        return None
+    entry = data.get("shapes", {}).get(name)
+    return None if entry is None else entry.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--family", type=int, default=1, choices=sorted(FAMILY_NAMES))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=48,
+                    help="rows of D per shape the oracle computes for the CPU baseline")
+    ap.add_argument("--per-shape-out", default="", help="also write per-shape results here")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has "
+              "no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import moe_grouped_gemm_block_amd as fp8bs
+    from moe_grouped_gemm_block_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    fp8bs._load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ---- inputs, resident in HBM ----
+    t0 = time.time()
+    problems = []
+    for desc in synth.workload_shapes(args.family):
+        p = synth.make(desc)
+        a = torch.from_numpy(p.A).to(dev)
+        sfa = fp8bs.sfa_mn_major(torch.from_numpy(p.SA)).to(dev)
+        b = torch.from_numpy(np.ascontiguousarray(p.B if p.kind != "dense" else p.B[0])).to(dev)
+        sfb = torch.from_numpy(np.ascontiguousarray(p.SB if p.kind != "dense" else p.SB[0])).to(dev)
+        if p.kind == "masked":
+            d = torch.empty((p.G, p.max_m, p.N), dtype=torch.bfloat16, device=dev)
+        else:
+            d = torch.empty((p.M, p.N), dtype=torch.bfloat16, device=dev)
+        extra = None
+        if p.kind == "contiguous":
+            extra = torch.from_numpy(p.layout).to(dev)
+        elif p.kind == "masked":
+            extra = torch.from_numpy(p.masked_m).to(dev)
+        problems.append(dict(desc=desc, p=p, a=a, sfa=sfa, b=b, sfb=sfb, d=d, extra=extra))
+    torch.cuda.synchronize()
+    gen_s = time.time() - t0
+
+    def launch(q):
+        p = q["p"]
+        if p.kind == "dense":
+            fp8bs.dense_nt(q["a"], q["sfa"], q["b"], q["sfb"], q["d"])
+        elif p.kind == "contiguous":
+            fp8bs.grouped_contiguous_nt(q["a"], q["sfa"], q["b"], q["sfb"], q["d"], q["extra"])
+        else:
+            fp8bs.grouped_masked_nt(q["a"], q["sfa"], q["b"], q["sfb"], q["d"], q["extra"],
+                                    expected_m=p.expected_m)
+
+    for _ in range(args.warmup):
+        for q in problems:
+            launch(q)
+    torch.cuda.synchronize()
+
+    # ---- timed region: K steps; events around every launch on the launch stream ----
+    stream = torch.cuda.current_stream(dev)
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in problems] for _ in range(args.steps)]
+    step_start = torch.cuda.Event(enable_timing=True)
+    step_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    step_start.record(stream)
+    for s in range(args.steps):
+        for i, q in enumerate(problems):
+            ev[s][i][0].record(stream)
+            launch(q)
+            ev[s][i][1].record(stream)
+    step_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = step_start.elapsed_time(step_end)
+    ms_per_step = total_ms / args.steps
+
+    flops_step = sum(q["p"].flops() for q in problems)
+    value = flops_step / (ms_per_step * 1e-3) / 1e12
+
+    per_shape = []
+    for i, q in enumerate(problems):
+        p = q["p"]
+        times = sorted(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps))
+        avg_ms = sum(times) / len(times)
+        med_ms = times[len(times) // 2]
+        tflops = p.flops() / (avg_ms * 1e-3) / 1e12
+        gbs = p.algorithmic_bytes() / (avg_ms * 1e-3) / 1e9
+        t_mfma = p.flops() / (PEAK_FP8_TFLOPS * 1e12)
+        t_hbm = p.algorithmic_bytes() / (PEAK_HBM_GBS * 1e9)
+        bound = "mfma" if t_mfma >= t_hbm else "hbm"
+        plan = fp8bs.describe_config({"dense": 0, "contiguous": 1, "masked": 2}[p.kind],
+                                     p.max_m if p.kind == "masked" else p.M, p.N, p.K, p.G,
+                                     p.expected_m)
+        per_shape.append(dict(
+            name=q["desc"]["name"], kind=p.kind, M=p.M, N=p.N, K=p.K, G=p.G,
+            valid_rows=p.valid_rows, gflop=p.flops() / 1e9, mbytes=p.algorithmic_bytes() / 1e6,
+            avg_us=avg_ms * 1e3, median_us=med_ms * 1e3, p10_us=times[len(times) // 10] * 1e3,
+            p90_us=times[(9 * len(times)) // 10] * 1e3, tflops=tflops, gbs=gbs, bound=bound,
+            roofline_frac=max(t_mfma, t_hbm) / (avg_ms * 1e-3), plan=plan))
+
+    dom = max(range(len(problems)), key=lambda i: per_shape[i]["avg_us"])
+    d = per_shape[dom]
+    if d["bound"] == "mfma":
+        roof = {"bound": "mfma", "achieved": d["tflops"], "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                "frac": d["tflops"] / PEAK_FP8_TFLOPS}
+    else:
+        roof = {"bound": "hbm", "achieved": d["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": d["gbs"] / PEAK_HBM_GBS}
+    roof["traffic"] = load_traffic(d["name"])
+    roof["kernel"] = d["name"]
+    roof["algorithmic_per_launch"] = {"gflop": d["gflop"], "mbytes": d["mbytes"]}
+    roof["avg_launch_us"] = d["avg_us"]
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(problems, args.cpu_rows)
+
+    out = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8e4m3", "data": "synthetic",
+        "config": {"workload": FAMILY_NAMES[args.family], "family": args.family,
+                   "shapes": [q["desc"]["name"] for q in problems],
+                   "gflop_per_step": flops_step / 1e9},
+        "roofline": roof, "cpu_baseline": cpu,
+        "per_shape": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in s.items()}
+                      for s in per_shape],
+        "wall_s": round(wall, 4), "input_gen_s": round(gen_s, 2),
+        "device": torch.cuda.get_device_name(dev),
+    }
+    if args.per_shape_out:
+        with open(args.per_shape_out, "w") as fh:
+            json.dump(out, fh, indent=1)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(problems, rows_per_shape: int):
+    """The oracle, untuned, on the host cores: the first `rows_per_shape` valid rows of D
+    (all N columns) of every shape of the step, timed; reported in TFLOP/s."""
+    import numpy as np
+
+    import oracle
+    from moe_grouped_gemm_block_amd import synth  # noqa: F401  (inputs already drawn)
+
+    flop = 0.0
+    t = 0.0
+    for q in problems:
+        p = q["p"]
+        valid = np.nonzero(_valid_rows(p))[0][:rows_per_shape]
+        rows = np.repeat(valid, p.N)
+        cols = np.tile(np.arange(p.N), valid.size)
+        grp = _row_groups(p)[rows]
+        B = p.B if p.kind != "dense" else p.B[0]
+        SB = p.SB if p.kind != "dense" else p.SB[0]
+        t0 = time.perf_counter()
+        oracle.points(p.A.reshape(-1, p.K), p.SA.reshape(-1, p.K // 128), B, SB, rows, grp, cols)
+        t += time.perf_counter() - t0
+        flop += 2.0 * rows.size * p.K
+    return {"value": flop / t / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "seconds": round(t, 3),
+            "sample": f"first {rows_per_shape} valid rows of D (all columns) of each shape in "
+                      f"the step, {flop / 1e9:.1f} GFLOP"}
+
+
+def _valid_rows(p):
+    import numpy as np
+    if p.kind == "dense":
+        return np.ones(p.M, bool)
+    if p.kind == "contiguous":
+        return (p.layout >= 0) & (p.layout < p.G)
+    v = np.clip(p.masked_m, 0, p.max_m)
+    return (np.arange(p.max_m)[None, :] < v[:, None]).reshape(-1)
+
+
+def _row_groups(p):
+    import numpy as np
+    if p.kind == "dense":
+        return np.zeros(p.M, np.int64)
+    if p.kind == "contiguous":
+        g = p.layout.astype(np.int64)
+        g[g < 0] = 0
+        return g
+    return np.repeat(np.arange(p.G), p.max_m)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,205 @@
+/*
+ * fp8bs.h -- C ABI of libfp8bs: block-scaled FP8 GEMM with BF16 output for
+ * AMD Instinct MI355X (gfx950 / CDNA4).
+ *
+ * The operation (all three entry points):
+ *
+ *     D[r][n] = bf16( sum_c  P_c(r,n) * SFA(r,c) * SFB(n/128,c) )
+ *     P_c(r,n) = sum_{k in [128c, 128c+128)} A[r][k] * B[n][k]
+ *
+ * A and B are OCP e4m3 (float8_e4m3fn: no infinities, max 448).  A carries one
+ * FP32 scale per row and per 128-wide K group ("1x128"); B carries one FP32
+ * scale per 128x128 block.  Each 128-K chunk's FP8 product is computed by the
+ * matrix cores into an FP32 partial, multiplied by the two scales and added
+ * into a separate FP32 accumulator (two-level accumulation), and the result is
+ * rounded once to BF16 (round to nearest even).
+ *
+ * Sources (web pages, cited by title and section):
+ *   - DeepGEMM README repost, lqnn.cn/news/60274, section "DeepGEMM": FP8
+ *     GEMM with the fine-grained scaling of DeepSeek-V3, dense and MoE grouped
+ *     GEMMs, two-level (promoted) accumulation on the CUDA cores.
+ *   - "DeepGEMM: kernel FP8 GEMM sạch và hiệu quả nhờ scaling chi tiết",
+ *     vi.news.hada.io/topic?id=19459:
+ *       section "Giao diện GEMM và ràng buộc layout": the NT form
+ *       D = C + A @ B.T (row-major A, column-major B), FP32 scale factors, the
+ *       LHS scale factors in a TMA-aligned, transposed (MN-major) layout;
+ *       section "Dense và Grouped GEMM": contiguous M-grouped layout (N, K fixed,
+ *       expert segments concatenated along M, each aligned to the M block size)
+ *       and the masked layout for graph-captured decoding, where the kernel
+ *       computes only the valid region given a device mask tensor;
+ *       section "Tiện ích và biến môi trường": set/get_num_sms,
+ *       get_mk_alignment_for_contiguous_layout, get_tma_aligned_size,
+ *       DG_PRINT_CONFIGS.
+ *   - "deepseek开源周第三天：DeepGEMM深度分析", pxiaoer.blog: the FP8 training
+ *     list (1x128 activation tiles, 128x128 weight blocks, FP32 accumulation).
+ *   The "+ C" term of the pages' naming is not part of this operation.
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers on the current HIP device; the
+ *     caller owns every buffer.  The library allocates nothing, keeps no
+ *     pointer after returning and never synchronises `stream`.
+ *   - Calls are asynchronous on `stream` (NULL = the default stream).  Buffers
+ *     must stay alive until the stream work completes.
+ *   - Inputs are read-only.  D is written only at valid rows (see each call)
+ *     and columns n < N; every other byte of D is left untouched.
+ *   - Pointers must be 16-byte aligned.  K must be a positive multiple of 128.
+ *   - SFA is stored MN-major ("transposed"): element (row r, K group c) lives at
+ *     sfa[c * ld + r] with ld = fp8bs_get_sfa_ld(rows).  SFB is row-major
+ *     [ceil(N/128)][K/128] per group.  D is row-major BF16 with row stride N.
+ *   - Errors are reported by the return value before anything is launched;
+ *     nothing is printed (unless FP8BS_PRINT_CONFIGS=1) and nothing aborts.
+ *     A launch failure reported by the HIP runtime maps to FP8BS_ERR_HIP.
+ *   - Thread-safe.  The only global state is the CU cap (fp8bs_set_num_cus).
+ *   - Graph-capturable: device-side group data (grouped_layout, masked_m) is
+ *     never read on the host.
+ */
+#ifndef FP8BS_H
+#define FP8BS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as HIP's stream handle. */
+struct ihipStream_t;
+typedef struct ihipStream_t* hipStream_t;
+
+typedef enum {
+    FP8BS_OK = 0,
+    FP8BS_ERR_SHAPE = 1,        /* a size violates the preconditions          */
+    FP8BS_ERR_POINTER = 2,      /* NULL or not 16-byte aligned                */
+    FP8BS_ERR_UNSUPPORTED = 3,  /* no kernel instance covers the request      */
+    FP8BS_ERR_HIP = 4           /* the HIP runtime reported an error          */
+} fp8bs_status;
+
+/* Layout codes for the planner queries. */
+typedef enum {
+    FP8BS_LAYOUT_DENSE = 0,
+    FP8BS_LAYOUT_CONTIGUOUS = 1,
+    FP8BS_LAYOUT_MASKED = 2
+} fp8bs_layout;
+
+/*
+ * Dense NT GEMM: D[m][n] = A[m][k] * B[n][k]^T with block scales.
+ *   a    e4m3 [m][k] row-major          sfa  f32 [k/128][fp8bs_get_sfa_ld(m)]
+ *   b    e4m3 [n][k] row-major          sfb  f32 [ceil(n/128)][k/128]
+ *   d    bf16 [m][n] row-major          every row 0 <= r < m is valid.
+ * m == 0 returns FP8BS_OK without launching.  (Section "Giao diện GEMM và
+ * ràng buộc layout" of the hada page: fp8_gemm_nt.)
+ */
+int fp8bs_dense_nt(const void* a, const float* sfa, const void* b, const float* sfb, void* d,
+                   int m, int n, int k, hipStream_t stream);
+
+/*
+ * M-grouped GEMM, contiguous layout: rows of several experts concatenated
+ * along M; expert g multiplies its rows by B[g].
+ *   a    e4m3 [m_total][k]              sfa  f32 [k/128][fp8bs_get_sfa_ld(m_total)]
+ *   b    e4m3 [num_groups][n][k]        sfb  f32 [num_groups][ceil(n/128)][k/128]
+ *   d    bf16 [m_total][n]
+ *   grouped_layout  int32 [m_total] (device): expert index of each row, -1 for
+ *        padding rows.  Each expert's segment starts at a multiple of
+ *        fp8bs_get_mk_alignment() (128) rows and every 128-row block holds rows
+ *        of a single expert followed only by padding.
+ * Valid rows: 0 <= grouped_layout[r] < num_groups.  Padding rows and rows with
+ * an index >= num_groups are not written.  m_total must be a multiple of 128.
+ * (Section "Dense và Grouped GEMM" of the hada page: contiguous layout.)
+ */
+int fp8bs_grouped_contiguous_nt(const void* a, const float* sfa, const void* b, const float* sfb,
+                                void* d, const int32_t* grouped_layout, int m_total, int n, int k,
+                                int num_groups, hipStream_t stream);
+
+/*
+ * M-grouped GEMM, masked layout: each expert owns a slot of max_m rows of
+ * which only the first masked_m[g] are valid; the host does not know
+ * masked_m (it lives on the device, e.g. inside a captured graph).
+ *   a    e4m3 [num_groups][max_m][k]    sfa  f32 [num_groups][k/128][fp8bs_get_sfa_ld(max_m)]
+ *   b    e4m3 [num_groups][n][k]        sfb  f32 [num_groups][ceil(n/128)][k/128]
+ *   d    bf16 [num_groups][max_m][n]
+ *   masked_m  int32 [num_groups] (device); values are clamped to [0, max_m].
+ *   expected_m  host hint of the typical masked_m (0 = unknown); it only
+ *        steers the tile-shape choice and never changes results.
+ * Valid rows: r < clamp(masked_m[g], 0, max_m) in slot g.  Other rows of D are
+ * not written.  (Section "Dense và Grouped GEMM" of the hada page: masked
+ * grouped GEMM for decoding under CUDA graphs.)
+ */
+int fp8bs_grouped_masked_nt(const void* a, const float* sfa, const void* b, const float* sfb,
+                            void* d, const int32_t* masked_m, int num_groups, int max_m,
+                            int expected_m, int n, int k, hipStream_t stream);
+
+/* Row alignment of expert segments in the contiguous layout (128).  Analogue
+ * of get_mk_alignment_for_contiguous_layout (hada page, section "Tiện ích và
+ * biến môi trường"). */
+int fp8bs_get_mk_alignment(void);
+
+/* Leading dimension, in floats, of the MN-major SFA for `rows` rows: rows
+ * rounded up to a multiple of 4 (16 bytes).  Analogue of get_tma_aligned_size
+ * (same section).  Returns -1 for rows < 0. */
+int64_t fp8bs_get_sfa_ld(int64_t rows);
+
+/* Cap on the compute units the persistent grid may occupy (0 = all).  It
+ * changes the launch shape, never the results.  Analogue of set_num_sms.
+ * Returns the previous cap, or -1 for n < 0. */
+int fp8bs_set_num_cus(int n);
+/* The current cap (0 = no cap). */
+int fp8bs_get_num_cus(void);
+
+/* Pins every later call to compiled instance i (see fp8bs_instance_info);
+ * -1 restores the planner's choice.  For testing and measuring tile shapes:
+ * the choice of instance changes speed, never results.  Returns the previous
+ * setting, or -2 for an index out of range. */
+int fp8bs_force_instance(int i);
+
+/* Planner result for one request, as chosen by the entry points. */
+typedef struct {
+    int block_m;        /* rows per output tile                               */
+    int block_n;        /* columns per output tile (may be non-power-of-two)  */
+    int waves_m;        /* wavefronts along M in a workgroup                  */
+    int waves_n;        /* wavefronts along N                                 */
+    int threads;        /* threads per workgroup                              */
+    int lds_bytes;      /* LDS per workgroup                                  */
+    int wg_per_cu;      /* workgroups resident per CU the planner assumes     */
+    int64_t tiles;      /* upper bound of output tiles in the schedule        */
+    int64_t grid;       /* persistent workgroups launched                     */
+    int raster;         /* m-blocks per raster group                          */
+    int instance;       /* index of the compiled kernel instance              */
+} fp8bs_plan;
+
+/*
+ * Host-only planner query (no device access): the configuration the entry
+ * point for `layout` would use for these sizes on a device with `num_cus`
+ * compute units.  For FP8BS_LAYOUT_DENSE `m` is M; for CONTIGUOUS it is
+ * m_total; for MASKED it is max_m (num_groups groups, expected_m hint).
+ * Returns FP8BS_OK and fills *out, or an error status.
+ */
+int fp8bs_plan_query(int layout, int64_t m, int n, int k, int num_groups, int expected_m,
+                     int num_cus, fp8bs_plan* out);
+
+/* Output tiles a (block_m x block_n) tiling has for a request: m-blocks x
+ * n-blocks (x num_groups for MASKED, where m is max_m).  Plain tile
+ * arithmetic, no device access; -1 on invalid arguments. */
+int64_t fp8bs_count_tiles(int layout, int64_t m, int n, int num_groups, int block_m, int block_n);
+
+/* Number of compiled kernel instances, and the shape of instance i (fields
+ * tiles, grid and raster are 0).  fp8bs_instance_info returns FP8BS_OK or
+ * FP8BS_ERR_UNSUPPORTED for an index out of range. */
+int fp8bs_num_instances(void);
+int fp8bs_instance_info(int i, fp8bs_plan* out);
+
+/* Human-readable summary of the plan for a request on the current device's CU
+ * count (respecting the cap), written to buf (NUL-terminated, truncated to
+ * len).  Analogue of DG_PRINT_CONFIGS; FP8BS_PRINT_CONFIGS=1 prints the same
+ * line to stderr at every call.  Returns the status of the planner. */
+int fp8bs_describe_config(int layout, int64_t m, int n, int k, int num_groups, int expected_m,
+                          char* buf, size_t len);
+
+/* Static description of a status code. */
+const char* fp8bs_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8BS_H */

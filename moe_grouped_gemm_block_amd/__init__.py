@@ -1,0 +1,261 @@
+"""Block-scaled FP8 GEMM (dense, MoE contiguous, MoE masked) for AMD MI355X.
+
+Thin Python binding of ``libfp8bs.so`` (C ABI declared in ``include/fp8bs.h``):
+argument checks and marshalling only -- every step of the computation runs in
+the library's HIP kernels.  PyTorch supplies device memory and the stream.
+
+The binding refuses to run without the compiled library; there is no fallback.
+Build it with ``python -m moe_grouped_gemm_block_amd.build``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+__all__ = [
+    "fp8bs_dense_nt", "fp8bs_grouped_contiguous_nt", "fp8bs_grouped_masked_nt",
+    "dense_nt", "grouped_contiguous_nt", "grouped_masked_nt",
+    "get_mk_alignment", "get_sfa_ld", "set_num_cus", "get_num_cus", "plan_query",
+    "describe_config", "count_tiles", "instances", "force_instance", "status_string", "sfa_mn_major", "library_path", "FP8BSError",
+    "LAYOUT_DENSE", "LAYOUT_CONTIGUOUS", "LAYOUT_MASKED",
+]
+
+LAYOUT_DENSE, LAYOUT_CONTIGUOUS, LAYOUT_MASKED = 0, 1, 2
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "lib", "libfp8bs.so")
+_lib = None
+
+
+class FP8BSError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+class _Plan(ctypes.Structure):
+    _fields_ = [("block_m", ctypes.c_int), ("block_n", ctypes.c_int), ("waves_m", ctypes.c_int),
+                ("waves_n", ctypes.c_int), ("threads", ctypes.c_int), ("lds_bytes", ctypes.c_int),
+                ("wg_per_cu", ctypes.c_int), ("tiles", ctypes.c_int64), ("grid", ctypes.c_int64),
+                ("raster", ctypes.c_int), ("instance", ctypes.c_int)]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing; build it with "
+                           "`python -m moe_grouped_gemm_block_amd.build` (no CPU fallback exists)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    lib.fp8bs_dense_nt.argtypes = [P, P, P, P, P, I, I, I, P]
+    lib.fp8bs_grouped_contiguous_nt.argtypes = [P, P, P, P, P, P, I, I, I, I, P]
+    lib.fp8bs_grouped_masked_nt.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P]
+    for f in ("fp8bs_dense_nt", "fp8bs_grouped_contiguous_nt", "fp8bs_grouped_masked_nt",
+              "fp8bs_get_mk_alignment", "fp8bs_set_num_cus", "fp8bs_get_num_cus",
+              "fp8bs_plan_query", "fp8bs_describe_config"):
+        getattr(lib, f).restype = I
+    lib.fp8bs_get_sfa_ld.argtypes = [I64]
+    lib.fp8bs_get_sfa_ld.restype = I64
+    lib.fp8bs_set_num_cus.argtypes = [I]
+    lib.fp8bs_plan_query.argtypes = [I, I64, I, I, I, I, I, ctypes.POINTER(_Plan)]
+    lib.fp8bs_describe_config.argtypes = [I, I64, I, I, I, I, ctypes.c_char_p, ctypes.c_size_t]
+    lib.fp8bs_count_tiles.argtypes = [I, I64, I, I, I, I]
+    lib.fp8bs_count_tiles.restype = I64
+    lib.fp8bs_num_instances.restype = I
+    lib.fp8bs_force_instance.argtypes = [I]
+    lib.fp8bs_force_instance.restype = I
+    lib.fp8bs_instance_info.argtypes = [I, ctypes.POINTER(_Plan)]
+    lib.fp8bs_instance_info.restype = I
+    lib.fp8bs_status_string.argtypes = [I]
+    lib.fp8bs_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return _load().fp8bs_status_string(int(status)).decode()
+
+
+def get_mk_alignment() -> int:
+    return int(_load().fp8bs_get_mk_alignment())
+
+
+def get_sfa_ld(rows: int) -> int:
+    return int(_load().fp8bs_get_sfa_ld(int(rows)))
+
+
+def set_num_cus(n: int) -> int:
+    return int(_load().fp8bs_set_num_cus(int(n)))
+
+
+def get_num_cus() -> int:
+    return int(_load().fp8bs_get_num_cus())
+
+
+def plan_query(layout: int, m: int, n: int, k: int, num_groups: int = 1, expected_m: int = 0,
+               num_cus: int = 256) -> dict:
+    plan = _Plan()
+    st = _load().fp8bs_plan_query(int(layout), int(m), int(n), int(k), int(num_groups),
+                                  int(expected_m), int(num_cus), ctypes.byref(plan))
+    if st != 0:
+        raise FP8BSError(st, "fp8bs_plan_query")
+    return {name: getattr(plan, name) for name, _ in _Plan._fields_}
+
+
+def count_tiles(layout: int, m: int, n: int, num_groups: int, block_m: int, block_n: int) -> int:
+    return int(_load().fp8bs_count_tiles(int(layout), int(m), int(n), int(num_groups),
+                                         int(block_m), int(block_n)))
+
+
+def instances() -> list:
+    lib = _load()
+    out = []
+    for i in range(lib.fp8bs_num_instances()):
+        plan = _Plan()
+        _check(lib.fp8bs_instance_info(i, ctypes.byref(plan)), "fp8bs_instance_info")
+        out.append({name: getattr(plan, name) for name, _ in _Plan._fields_})
+    return out
+
+
+def force_instance(i: int) -> int:
+    """Pin every later call to compiled instance i (-1 = planner's choice); returns the previous."""
+    prev = int(_load().fp8bs_force_instance(int(i)))
+    if prev == -2:
+        raise ValueError(f"no compiled instance {i}")
+    return prev
+
+
+def describe_config(layout: int, m: int, n: int, k: int, num_groups: int = 1,
+                    expected_m: int = 0) -> str:
+    buf = ctypes.create_string_buffer(512)
+    st = _load().fp8bs_describe_config(int(layout), int(m), int(n), int(k), int(num_groups),
+                                       int(expected_m), buf, 512)
+    if st != 0:
+        raise FP8BSError(st, "fp8bs_describe_config")
+    return buf.value.decode()
+
+
+# ---- tensor marshalling ----------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dev_ptr(t, name, dtypes, ndim=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _fp8_dtypes():
+    torch = _torch()
+    return (torch.uint8, torch.float8_e4m3fn)
+
+
+def _bf16_dtypes():
+    torch = _torch()
+    return (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _stream_handle(stream, device):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def sfa_mn_major(sa, rows_ld: Optional[int] = None):
+    """Logical A scales [..., rows, K/128] -> MN-major storage [..., K/128, ld(rows)].
+
+    Works on torch tensors (any device) and returns a contiguous tensor whose
+    padding columns are zero.  Layout helper, analogous to the pages'
+    transform_sf_into_required_layout."""
+    torch = _torch()
+    rows, kb = sa.shape[-2], sa.shape[-1]
+    ld = get_sfa_ld(rows) if rows_ld is None else rows_ld
+    out = torch.zeros(*sa.shape[:-2], kb, ld, dtype=torch.float32, device=sa.device)
+    out[..., :, :rows] = sa.transpose(-1, -2)
+    return out
+
+
+def _check(st: int, where: str):
+    if st != 0:
+        raise FP8BSError(st, where)
+
+
+def fp8bs_dense_nt(a, sfa, b, sfb, d, stream=None):
+    """D[m][n] = A[m][k] * B[n][k]^T with 1x128 A scales and 128x128 B scales.
+
+    a: e4m3 [m][k]; sfa: f32 MN-major [k/128][ld(m)]; b: e4m3 [n][k];
+    sfb: f32 [ceil(n/128)][k/128]; d: bf16 [m][n] (written)."""
+    m, k = a.shape
+    n = b.shape[0]
+    kb = k // 128 if k % 128 == 0 else -1
+    args = (_dev_ptr(a, "a", _fp8_dtypes(), 2), _dev_ptr(sfa, "sfa", (_torch().float32,)),
+            _dev_ptr(b, "b", _fp8_dtypes(), 2), _dev_ptr(sfb, "sfb", (_torch().float32,)),
+            _dev_ptr(d, "d", _bf16_dtypes(), 2))
+    if b.shape[1] != k or tuple(d.shape) != (m, n):
+        raise ValueError("shape mismatch between a, b and d")
+    if kb > 0 and (sfa.numel() != kb * get_sfa_ld(m) or sfb.numel() != ((n + 127) // 128) * kb):
+        raise ValueError("scale tensor sizes do not match the shapes")
+    _check(_load().fp8bs_dense_nt(*args, m, n, k, _stream_handle(stream, a.device)),
+           "fp8bs_dense_nt")
+
+
+def fp8bs_grouped_contiguous_nt(a, sfa, b, sfb, d, grouped_layout, stream=None):
+    """Contiguous MoE layout: a [m_total][k], b [g][n][k], grouped_layout int32 [m_total]."""
+    torch = _torch()
+    m, k = a.shape
+    g, n = b.shape[0], b.shape[1]
+    kb = k // 128 if k % 128 == 0 else -1
+    args = (_dev_ptr(a, "a", _fp8_dtypes(), 2), _dev_ptr(sfa, "sfa", (torch.float32,)),
+            _dev_ptr(b, "b", _fp8_dtypes(), 3), _dev_ptr(sfb, "sfb", (torch.float32,)),
+            _dev_ptr(d, "d", _bf16_dtypes(), 2),
+            _dev_ptr(grouped_layout, "grouped_layout", (torch.int32,), 1))
+    if b.shape[2] != k or tuple(d.shape) != (m, n) or grouped_layout.shape[0] != m:
+        raise ValueError("shape mismatch between a, b, d and grouped_layout")
+    if kb > 0 and (sfa.numel() != kb * get_sfa_ld(m) or sfb.numel() != g * ((n + 127) // 128) * kb):
+        raise ValueError("scale tensor sizes do not match the shapes")
+    _check(_load().fp8bs_grouped_contiguous_nt(*args, m, n, k, g, _stream_handle(stream, a.device)),
+           "fp8bs_grouped_contiguous_nt")
+
+
+def fp8bs_grouped_masked_nt(a, sfa, b, sfb, d, masked_m, expected_m: int = 0, stream=None):
+    """Masked MoE layout: a [g][max_m][k], b [g][n][k], d [g][max_m][n], masked_m int32 [g]."""
+    torch = _torch()
+    g, max_m, k = a.shape
+    n = b.shape[1]
+    kb = k // 128 if k % 128 == 0 else -1
+    args = (_dev_ptr(a, "a", _fp8_dtypes(), 3), _dev_ptr(sfa, "sfa", (torch.float32,)),
+            _dev_ptr(b, "b", _fp8_dtypes(), 3), _dev_ptr(sfb, "sfb", (torch.float32,)),
+            _dev_ptr(d, "d", _bf16_dtypes(), 3), _dev_ptr(masked_m, "masked_m", (torch.int32,), 1))
+    if b.shape[0] != g or b.shape[2] != k or tuple(d.shape) != (g, max_m, n) or masked_m.shape[0] != g:
+        raise ValueError("shape mismatch between a, b, d and masked_m")
+    if kb > 0 and (sfa.numel() != g * kb * get_sfa_ld(max_m)
+                   or sfb.numel() != g * ((n + 127) // 128) * kb):
+        raise ValueError("scale tensor sizes do not match the shapes")
+    _check(_load().fp8bs_grouped_masked_nt(*args, g, max_m, int(expected_m), n, k,
+                                           _stream_handle(stream, a.device)),
+           "fp8bs_grouped_masked_nt")
+
+
+dense_nt = fp8bs_dense_nt
+grouped_contiguous_nt = fp8bs_grouped_contiguous_nt
+grouped_masked_nt = fp8bs_grouped_masked_nt

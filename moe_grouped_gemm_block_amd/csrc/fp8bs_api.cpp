@@ -1,0 +1,155 @@
+// fp8bs_api.cpp -- the C ABI of libfp8bs (declared in include/fp8bs.h):
+// argument checks, the planner call and the kernel launch on the caller's
+// stream.  No allocation, no synchronisation, no host reads of device data.
+#include <hip/hip_runtime.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "fp8bs_internal.h"
+
+namespace {
+
+std::atomic<int> g_cu_cap{0};
+std::atomic<int> g_forced_instance{-1};
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_dev_cus[kMaxDevices];   // 0 = not queried yet
+
+bool print_configs() {
+    static const int on = [] {
+        const char* e = getenv("FP8BS_PRINT_CONFIGS");
+        return (e && e[0] && e[0] != '0') ? 1 : 0;
+    }();
+    return on != 0;
+}
+
+// Compute units of the current device, capped by fp8bs_set_num_cus; 0 on error.
+int current_num_cus() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    int cus = (dev >= 0 && dev < kMaxDevices) ? g_dev_cus[dev].load(std::memory_order_relaxed) : 0;
+    if (cus == 0) {
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return 0;
+        if (dev >= 0 && dev < kMaxDevices) g_dev_cus[dev].store(cus, std::memory_order_relaxed);
+    }
+    const int cap = g_cu_cap.load(std::memory_order_relaxed);
+    return (cap > 0 && cap < cus) ? cap : cus;
+}
+
+bool aligned16(const void* p) { return p && ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return p && ((uintptr_t)p & 3u) == 0; }
+
+void format_plan(const fp8bs::Plan& pl, int layout, int64_t m, int n, int k, int g,
+                 int expected_m, int cus, char* buf, size_t len) {
+    static const char* names[3] = {"dense", "contiguous", "masked"};
+    snprintf(buf, len,
+             "fp8bs %s m=%lld n=%d k=%d groups=%d expected_m=%d cus=%d -> block %dx%d "
+             "waves %dx%d threads %d lds %dB wg/cu %d tiles %lld grid %lld raster %d instance %d",
+             names[layout], (long long)m, n, k, g, expected_m, cus, pl.shape.block_m,
+             pl.shape.block_n, pl.shape.waves_m, pl.shape.waves_n,
+             64 * pl.shape.waves_m * pl.shape.waves_n, pl.shape.lds_bytes, pl.shape.wg_per_cu,
+             (long long)pl.tiles, (long long)pl.grid, pl.raster, pl.instance);
+}
+
+int run(int layout, const void* a, const float* sfa, const void* b, const float* sfb, void* d,
+        const int32_t* group_data, int64_t m, int n, int k, int num_groups, int expected_m,
+        hipStream_t stream) {
+    int st = fp8bs::validate_sizes(layout, m, n, k, num_groups);
+    if (st != FP8BS_OK) return st;
+    if (!aligned16(a) || !aligned16(sfa) || !aligned16(b) || !aligned16(sfb) || !aligned16(d))
+        return FP8BS_ERR_POINTER;
+    if (layout != fp8bs::kDense && !aligned4(group_data)) return FP8BS_ERR_POINTER;
+    if (m == 0) return FP8BS_OK;
+    const int cus = current_num_cus();
+    if (cus <= 0) return FP8BS_ERR_HIP;
+    fp8bs::Plan pl;
+    st = fp8bs::plan_request(layout, m, n, k, num_groups, expected_m, cus, &pl);
+    if (st != FP8BS_OK) return st;
+    const int forced = g_forced_instance.load(std::memory_order_relaxed);
+    if (forced >= 0) {
+        st = fp8bs::plan_instance(forced, layout, m, n, num_groups, cus, &pl);
+        if (st != FP8BS_OK) return st;
+    }
+    if (print_configs()) {
+        char line[512];
+        format_plan(pl, layout, m, n, k, num_groups, expected_m, cus, line, sizeof line);
+        fprintf(stderr, "%s\n", line);
+    }
+    fp8bs::GemmParams p;
+    p.a = (const uint8_t*)a;
+    p.sfa = sfa;
+    p.b = (const uint8_t*)b;
+    p.sfb = sfb;
+    p.d = (uint16_t*)d;
+    p.grouped_layout = layout == fp8bs::kContiguous ? group_data : nullptr;
+    p.masked_m = layout == fp8bs::kMasked ? group_data : nullptr;
+    p.m = (int)m;
+    p.n = n;
+    p.k = k;
+    p.num_groups = num_groups;
+    p.sfa_ld = (int)fp8bs_get_sfa_ld(m);
+    p.m_blocks = (int)((m + pl.shape.block_m - 1) / pl.shape.block_m);
+    p.n_blocks = (n + pl.shape.block_n - 1) / pl.shape.block_n;
+    p.tiles = (int)pl.tiles;
+    p.raster = pl.raster;
+    const int err = fp8bs::launch_instance(pl, layout, p, stream);
+    return err == (int)hipSuccess ? FP8BS_OK : FP8BS_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp8bs_dense_nt(const void* a, const float* sfa, const void* b, const float* sfb, void* d,
+                   int m, int n, int k, hipStream_t stream) {
+    return run(fp8bs::kDense, a, sfa, b, sfb, d, nullptr, m, n, k, 1, 0, stream);
+}
+
+int fp8bs_grouped_contiguous_nt(const void* a, const float* sfa, const void* b, const float* sfb,
+                                void* d, const int32_t* grouped_layout, int m_total, int n, int k,
+                                int num_groups, hipStream_t stream) {
+    return run(fp8bs::kContiguous, a, sfa, b, sfb, d, grouped_layout, m_total, n, k, num_groups,
+               0, stream);
+}
+
+int fp8bs_grouped_masked_nt(const void* a, const float* sfa, const void* b, const float* sfb,
+                            void* d, const int32_t* masked_m, int num_groups, int max_m,
+                            int expected_m, int n, int k, hipStream_t stream) {
+    if (num_groups < 1) return FP8BS_ERR_SHAPE;
+    return run(fp8bs::kMasked, a, sfa, b, sfb, d, masked_m, max_m, n, k, num_groups, expected_m,
+               stream);
+}
+
+int fp8bs_set_num_cus(int n) {
+    if (n < 0) return -1;
+    return g_cu_cap.exchange(n);
+}
+
+int fp8bs_get_num_cus(void) { return g_cu_cap.load(); }
+
+int fp8bs_force_instance(int i) {
+    if (i < -1 || i >= fp8bs::kNumInstances) return -2;
+    return g_forced_instance.exchange(i);
+}
+
+int fp8bs_describe_config(int layout, int64_t m, int n, int k, int num_groups, int expected_m,
+                          char* buf, size_t len) {
+    if (!buf || len == 0) return FP8BS_ERR_POINTER;
+    if (layout < 0 || layout > 2) return FP8BS_ERR_UNSUPPORTED;
+    const int g = layout == fp8bs::kDense ? 1 : num_groups;
+    const int cus = current_num_cus();
+    if (cus <= 0) return FP8BS_ERR_HIP;
+    fp8bs::Plan pl;
+    const int st = fp8bs::plan_request(layout, m, n, k, g, expected_m, cus, &pl);
+    if (st != FP8BS_OK) {
+        snprintf(buf, len, "%s", fp8bs_status_string(st));
+        return st;
+    }
+    format_plan(pl, layout, m, n, k, g, expected_m, cus, buf, len);
+    return FP8BS_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,67 @@
+// fp8bs_internal.h -- types shared by the host planner, the C ABI and the
+// kernel instances of libfp8bs.  Not part of the public interface.
+#pragma once
+#include <stdint.h>
+
+#include "../../include/fp8bs.h"
+
+namespace fp8bs {
+
+enum Layout : int { kDense = 0, kContiguous = 1, kMasked = 2 };
+
+// Shape of one compiled kernel instance: an output tile of block_m x block_n
+// computed by waves_m x waves_n wavefronts (64 lanes each), each owning a
+// (block_m / waves_m) x (block_n / waves_n) sub-tile made of 16x16 MFMA tiles.
+struct InstanceShape {
+    int block_m, block_n, waves_m, waves_n;
+    int wg_per_cu;       // workgroups per CU the launch assumes (LDS / register bound)
+    int lds_bytes;
+};
+
+// The instance table (defined next to the kernels, read by the planner).
+extern const InstanceShape kInstances[];
+extern const int kNumInstances;
+
+// Everything a kernel needs; plain values and device pointers.
+struct GemmParams {
+    const uint8_t* a;
+    const float* sfa;
+    const uint8_t* b;
+    const float* sfb;
+    uint16_t* d;
+    const int32_t* grouped_layout;   // contiguous only
+    const int32_t* masked_m;         // masked only
+    int m;              // dense: M; contiguous: m_total; masked: max_m (rows per slot)
+    int n, k;
+    int num_groups;
+    int sfa_ld;         // leading dimension of the MN-major SFA (per slot for masked)
+    int m_blocks;       // ceil(m / block_m)
+    int n_blocks;       // ceil(n / block_n)
+    int tiles;          // (num_groups for masked) x m_blocks x n_blocks
+    int raster;         // m-blocks per raster group
+};
+
+struct Plan {
+    int instance;
+    InstanceShape shape;
+    int64_t tiles;
+    int64_t grid;
+    int raster;
+};
+
+// Host planner: deterministic choice of an instance and launch shape.
+// Returns FP8BS_OK or an error status.  No device access.
+int plan_request(int layout, int64_t m, int n, int k, int num_groups, int expected_m,
+                 int num_cus, Plan* out);
+
+// Launch shape for a given instance (used when an instance is pinned).
+int plan_instance(int instance, int layout, int64_t m, int n, int num_groups, int num_cus,
+                  Plan* out);
+
+// Validates sizes for an entry point (FP8BS_OK or FP8BS_ERR_SHAPE).
+int validate_sizes(int layout, int64_t m, int n, int k, int num_groups);
+
+// Launches instance `plan.instance` for `layout`; returns a hipError_t value.
+int launch_instance(const Plan& plan, int layout, const GemmParams& p, hipStream_t stream);
+
+}  // namespace fp8bs

@@ -1,0 +1,146 @@
+"""Host-side checks of the C ABI library (no GPU needed): it loads, exports every
+function declared in include/fp8bs.h, and its planner, helpers and argument
+validation behave as documented.  No call here launches a kernel."""
+import ctypes
+import json
+import os
+import re
+import subprocess
+
+import pytest
+
+import moe_grouped_gemm_block_amd as fp8bs
+from moe_grouped_gemm_block_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8bs.h")
+OK, ERR_SHAPE, ERR_POINTER, ERR_UNSUPPORTED, ERR_HIP = 0, 1, 2, 3, 4
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp8bs_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = _declared_functions()
+    assert {"fp8bs_dense_nt", "fp8bs_grouped_contiguous_nt", "fp8bs_grouped_masked_nt"} <= set(names)
+    lib = ctypes.CDLL(fp8bs.library_path())
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", fp8bs.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+
+
+def test_status_strings_and_helpers():
+    assert fp8bs.status_string(OK) == "ok"
+    for st in (ERR_SHAPE, ERR_POINTER, ERR_UNSUPPORTED, ERR_HIP):
+        assert fp8bs.status_string(st) not in ("ok", "unknown status")
+    assert fp8bs.status_string(99) == "unknown status"
+    assert fp8bs.get_mk_alignment() == 128
+    assert [fp8bs.get_sfa_ld(r) for r in (0, 1, 3, 4, 5, 4096, 4097)] == [0, 4, 4, 4, 8, 4096, 4100]
+    assert fp8bs.get_sfa_ld(-1) == -1
+
+
+def test_page_tile_count_example():
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "sm_fill_example.json")))
+    for c in g["cases"]:
+        assert fp8bs.count_tiles(fp8bs.LAYOUT_DENSE, g["m"], g["n"], 1, c["block_m"], c["block_n"]) \
+            == c["tiles"]
+    shapes = {(i["block_m"], i["block_n"]) for i in fp8bs.instances()}
+    assert (128, 112) in shapes                    # the page's non-power-of-two BLOCK_N is compiled
+    # with the page's 132 SMs the planner does not settle for the 112-tile 128x128 tiling
+    p = fp8bs.plan_query(fp8bs.LAYOUT_DENSE, 256, 7168, 7168, num_cus=132)
+    assert p["tiles"] >= 128 and (p["block_m"], p["block_n"]) != (128, 128)
+
+
+def test_planner_fills_256_cus_for_the_decode_tile_case():
+    p = fp8bs.plan_query(fp8bs.LAYOUT_DENSE, 256, 7168, 7168, num_cus=256)
+    assert p["tiles"] >= 256
+    assert p["grid"] <= 256 * p["wg_per_cu"]
+
+
+def test_planner_is_deterministic_and_consistent():
+    for fam in range(5):
+        for d in synth.workload_shapes(fam):
+            layout = {"dense": 0, "contiguous": 1, "masked": 2}[d["kind"]]
+            m = d.get("M", 0) if layout == 0 else (33152 if layout == 1 else d["max_m"])
+            g = d.get("G", 1)
+            q1 = fp8bs.plan_query(layout, m, d["N"], d["K"], g, d.get("expected_m", 0), 256)
+            q2 = fp8bs.plan_query(layout, m, d["N"], d["K"], g, d.get("expected_m", 0), 256)
+            assert q1 == q2
+            assert 1 <= q1["grid"] <= q1["tiles"]
+            assert q1["tiles"] == fp8bs.count_tiles(layout, m, d["N"], g, q1["block_m"], q1["block_n"])
+            if layout == 1:
+                assert 128 % q1["block_m"] == 0
+            assert q1["threads"] == 64 * q1["waves_m"] * q1["waves_n"]
+
+
+def test_every_instance_is_well_formed():
+    insts = fp8bs.instances()
+    assert len(insts) >= 8
+    for i in insts:
+        assert i["block_m"] % (16 * i["waves_m"]) == 0 and i["block_n"] % (16 * i["waves_n"]) == 0
+        assert i["lds_bytes"] * i["wg_per_cu"] <= 160 * 1024
+    assert any(i["block_n"] & (i["block_n"] - 1) for i in insts)      # a non-power-of-two BLOCK_N
+
+
+def test_planner_rejects_bad_sizes():
+    with pytest.raises(fp8bs.FP8BSError):
+        fp8bs.plan_query(0, 128, 2112, 100)
+    with pytest.raises(fp8bs.FP8BSError):
+        fp8bs.plan_query(1, 100, 256, 128, 2)
+    with pytest.raises(fp8bs.FP8BSError):
+        fp8bs.plan_query(2, 64, 256, 128, 0)
+    with pytest.raises(fp8bs.FP8BSError):
+        fp8bs.plan_query(0, 64, 0, 128)
+
+
+class _Fake:
+    """16-byte aligned host buffer used as an opaque pointer; calls below fail validation
+    (or have nothing to do) before anything could touch it."""
+
+    def __init__(self):
+        self.buf = ctypes.create_string_buffer(256)
+        self.ptr = (ctypes.addressof(self.buf) + 15) // 16 * 16
+
+
+def test_entry_points_validate_before_launching():
+    lib = fp8bs._load()
+    f = _Fake().ptr
+    # K not a multiple of 128, n < 1, m < 0
+    assert lib.fp8bs_dense_nt(f, f, f, f, f, 128, 2112, 100, None) == ERR_SHAPE
+    assert lib.fp8bs_dense_nt(f, f, f, f, f, 128, 0, 128, None) == ERR_SHAPE
+    assert lib.fp8bs_dense_nt(f, f, f, f, f, -1, 16, 128, None) == ERR_SHAPE
+    # NULL and misaligned pointers
+    assert lib.fp8bs_dense_nt(None, f, f, f, f, 128, 16, 128, None) == ERR_POINTER
+    assert lib.fp8bs_dense_nt(f, f, f + 4, f, f, 128, 16, 128, None) == ERR_POINTER
+    # contiguous: m_total not a multiple of 128, no groups, missing layout
+    assert lib.fp8bs_grouped_contiguous_nt(f, f, f, f, f, f, 100, 16, 128, 2, None) == ERR_SHAPE
+    assert lib.fp8bs_grouped_contiguous_nt(f, f, f, f, f, f, 128, 16, 128, 0, None) == ERR_SHAPE
+    assert lib.fp8bs_grouped_contiguous_nt(f, f, f, f, f, None, 128, 16, 128, 2, None) == ERR_POINTER
+    # masked: no groups, bad K, missing mask
+    assert lib.fp8bs_grouped_masked_nt(f, f, f, f, f, f, 0, 64, 0, 16, 128, None) == ERR_SHAPE
+    assert lib.fp8bs_grouped_masked_nt(f, f, f, f, f, f, 2, 64, 0, 16, 129, None) == ERR_SHAPE
+    assert lib.fp8bs_grouped_masked_nt(f, f, f, f, f, None, 2, 64, 0, 16, 128, None) == ERR_POINTER
+    # nothing to do: m == 0 / max_m == 0 return OK without launching
+    assert lib.fp8bs_dense_nt(f, f, f, f, f, 0, 16, 128, None) == OK
+    assert lib.fp8bs_grouped_contiguous_nt(f, f, f, f, f, f, 0, 16, 128, 2, None) == OK
+    assert lib.fp8bs_grouped_masked_nt(f, f, f, f, f, f, 2, 0, 0, 16, 128, None) == OK
+
+
+def test_cu_cap_and_forced_instance_setters():
+    prev = fp8bs.set_num_cus(100)
+    try:
+        assert fp8bs.get_num_cus() == 100
+        assert fp8bs._load().fp8bs_set_num_cus(-3) == -1
+    finally:
+        fp8bs.set_num_cus(prev)
+    assert fp8bs.force_instance(0) == -1
+    assert fp8bs.force_instance(-1) == 0
+    with pytest.raises(ValueError):
+        fp8bs.force_instance(10 ** 6)

@@ -1,0 +1,192 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Small shapes are compared whole (several tiles and ragged tails in M and N);
+every compiled kernel instance is exercised for every layout it supports.
+Rows that must not be written are checked bit-exactly against the sentinel.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import moe_grouped_gemm_block_amd as fp8bs
+from moe_grouped_gemm_block_amd import synth
+from _helpers import (SENTINEL, DeviceProblem, check_full, check_values, oracle_full,
+                      bf16_bits_to_f64)
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(autouse=True)
+def _planner_choice():
+    fp8bs.force_instance(-1)
+    yield
+    fp8bs.force_instance(-1)
+
+
+def _run_and_check(p, what):
+    _say(f"[gpu] {what}: {p.kind} M={p.M} N={p.N} K={p.K} G={p.G}")
+    dp = DeviceProblem(p)
+    dp.run()
+    gpu = dp.result()
+    ref = oracle_full(p)
+    return check_full(p, gpu, ref, what)
+
+
+def _instances(layout):
+    out = []
+    for inst in fp8bs.instances():
+        if layout == fp8bs.LAYOUT_CONTIGUOUS and 128 % inst["block_m"] != 0:
+            continue
+        out.append(inst["instance"])
+    return out
+
+
+N_INST = 11
+
+
+@pytest.mark.parametrize("inst", range(N_INST))
+def test_dense_every_instance(inst):
+    fp8bs.force_instance(inst)
+    p = synth.make_dense(300, 500, 512, seed=11 + inst)
+    _run_and_check(p, f"dense inst {inst}")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 128), (5, 2112, 256), (129, 129, 128), (64, 7168, 384),
+                                   (256, 7168, 256), (1000, 96, 1280), (33, 4096, 128)])
+def test_dense_planner_shapes(M, N, K):
+    p = synth.make_dense(M, N, K, seed=M * 7 + N + K, outlier_frac=0.01)
+    _run_and_check(p, f"dense {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("inst", range(N_INST))
+def test_contiguous_every_instance(inst):
+    if inst not in _instances(fp8bs.LAYOUT_CONTIGUOUS):
+        pytest.skip("block_m does not divide the 128-row alignment")
+    fp8bs.force_instance(inst)
+    p = synth.make_contiguous(4, 300, 384, seed=31 + inst, counts=[200, 0, 1, 129])
+    _run_and_check(p, f"contiguous inst {inst}")
+
+
+def test_contiguous_planner_multinomial():
+    p = synth.make_contiguous(8, 520, 256, seed=41, total_rows=1500)
+    _run_and_check(p, "contiguous multinomial")
+
+
+@pytest.mark.parametrize("inst", range(N_INST))
+def test_masked_every_instance(inst):
+    fp8bs.force_instance(inst)
+    p = synth.make_masked(5, 200, 300, 384, seed=51 + inst, masked_m=[0, 200, 1, 77, 129])
+    _run_and_check(p, f"masked inst {inst}")
+
+
+def test_masked_clamps_out_of_range_counts():
+    p = synth.make_masked(4, 64, 200, 256, seed=61, masked_m=[-5, 1000, 64, 3])
+    _run_and_check(p, "masked clamp")
+
+
+def test_masked_planner_expected_m():
+    p = synth.make_masked(16, 256, 384, 512, seed=62, expected_m=128)
+    _run_and_check(p, "masked expected_m")
+
+
+# ---- closed forms, bit-exact on the GPU too ------------------------------------
+
+def test_constant_inputs_bit_exact():
+    M, N, K = 200, 300, 7168
+    p = synth.make_dense(M, N, K, seed=0)
+    p.A[:] = 0x38                                     # 1.0
+    p.B[:] = 0x38
+    p.SA[:] = 1.0
+    p.SB[:] = 1.0
+    dp = DeviceProblem(p)
+    dp.run()
+    gpu = dp.result()
+    assert np.all(gpu == 0x45E0)                      # 7168
+
+
+def test_one_hot_rows_bit_exact():
+    rng = np.random.default_rng(3)
+    M, N, K = 40, 300, 1024
+    p = synth.make_dense(M, N, K, seed=3)
+    pi = rng.choice(K, size=M, replace=False)
+    p.A[:] = 0
+    p.A[np.arange(M), pi] = 0x38
+    p.SA[:] = (2.0 ** rng.integers(-3, 4, size=p.SA.shape)).astype(np.float32)
+    p.SB[:] = (2.0 ** rng.integers(-3, 4, size=p.SB.shape)).astype(np.float32)
+    dp = DeviceProblem(p)
+    dp.run()
+    assert np.array_equal(dp.result(), oracle_full(p))
+
+
+def test_scale_shift_invariance_bit_exact():
+    """Doubling every byte value of one 1x128 group and halving its scale leaves D
+    unchanged bit for bit (FP32 MFMA sums of FP8 products scale exactly)."""
+    p = synth.make_dense(130, 260, 512, seed=5)
+    rng = np.random.default_rng(5)
+    grp = rng.integers(0, 0x70, size=128, dtype=np.uint8) | (rng.integers(0, 2, 128, dtype=np.uint8) << 7)
+    p.A[7, 256:384] = grp                             # exponent field <= 13: doubling stays exact
+    dp = DeviceProblem(p)
+    dp.run()
+    d0 = dp.result()
+    v = torch.from_numpy(grp.copy()).view(torch.float8_e4m3fn).to(torch.float32)
+    dbl = (v * 2).to(torch.float8_e4m3fn)
+    assert torch.equal(dbl.to(torch.float32), v * 2)
+    p.A[7, 256:384] = dbl.view(torch.uint8).numpy()
+    p.SA[7, 2] /= 2
+    dp2 = DeviceProblem(p)
+    dp2.run()
+    assert np.array_equal(dp2.result(), d0)
+
+
+def test_run_to_run_determinism():
+    p = synth.make_dense(512, 1000, 1024, seed=6)
+    dp = DeviceProblem(p)
+    dp.run()
+    d0 = dp.result()
+    dp.reset()
+    dp.run()
+    assert np.array_equal(dp.result(), d0)
+
+
+def test_poisoned_padding_and_masked_rows_stay_out():
+    pc = synth.make_contiguous(3, 200, 256, seed=71, counts=[100, 30, 129])
+    pad = pc.layout < 0
+    pc.A[pad] = 0x7F                                  # e4m3 NaN
+    pc.SA[pad] = np.nan
+    dp = DeviceProblem(pc)
+    dp.run()
+    check_full(pc, dp.result(), oracle_full(pc), "poisoned contiguous")
+    pm = synth.make_masked(3, 96, 200, 256, seed=72, masked_m=[5, 96, 40])
+    for g, v in enumerate(pm.masked_m):
+        pm.A[g, v:] = 0x7F
+        pm.SA[g, v:] = np.nan
+    dp = DeviceProblem(pm)
+    dp.run()
+    check_full(pm, dp.result(), oracle_full(pm), "poisoned masked")
+
+
+def test_stream_argument_is_honoured():
+    p = synth.make_dense(64, 256, 256, seed=8)
+    dp = DeviceProblem(p)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        dp.run(stream=s)
+    s.synchronize()
+    check_full(p, dp.d.cpu().numpy().view(np.uint16), oracle_full(p), "side stream")
+
+
+def test_zero_rows_is_a_no_op():
+    buf = torch.zeros(64, dtype=torch.float32, device="cuda")
+    ptr = buf.data_ptr()
+    # m == 0: nothing to do and nothing launched; the pointers are never dereferenced
+    assert fp8bs._load().fp8bs_dense_nt(ptr, ptr, ptr, ptr, ptr, 0, 16, 128, None) == 0
+    assert fp8bs._load().fp8bs_grouped_masked_nt(ptr, ptr, ptr, ptr, ptr, ptr, 2, 0, 0, 16, 128,
+                                                 None) == 0
+    torch.cuda.synchronize()
