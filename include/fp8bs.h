@@ -43,6 +43,8 @@
  *   - Inputs are read-only.  D is written only at valid rows (see each call)
  *     and columns n < N; every other byte of D is left untouched.
  *   - Pointers must be 16-byte aligned.  K must be a positive multiple of 128.
+ *     One A slot (rows x K bytes: m, m_total or max_m rows) and one B group
+ *     (N x K bytes) must each be smaller than 4 GiB.
  *   - SFA is stored MN-major ("transposed"): element (row r, K group c) lives at
  *     sfa[c * ld + r] with ld = fp8bs_get_sfa_ld(rows).  SFB is row-major
  *     [ceil(N/128)][K/128] per group.  D is row-major BF16 with row stride N.

@@ -1,26 +1,36 @@
 // fp8bs_gemm.hip -- the block-scaled FP8 GEMM kernel for gfx950 (CDNA4).
 //
 // One kernel template serves the dense, contiguous-grouped and masked-grouped
-// layouts (the DeepGEMM README repost, lqnn.cn/news/60274, "DeepGEMM" and
-// "优化技术": one core kernel and one block scheduler for grouped and
-// non-grouped GEMMs).  Per output tile and per 128-wide K chunk:
+// layouts (the DeepGEMM README repost, lqnn.cn/news/60274, sections
+// "DeepGEMM" and "优化技术": one core kernel and one block scheduler for the
+// grouped and non-grouped GEMMs).  Per output tile and per 128-wide K chunk:
 //
-//   1. the A tile (block_m x 128 e4m3) and the B tile (block_n x 128 e4m3) are
-//      staged in LDS (double buffered, 16-byte XOR swizzle per 128-byte row);
-//   2. each wavefront computes its 16x16 sub-tiles with one
-//      v_mfma_f32_16x16x128_f8f6f4 each (OCP e4m3 x e4m3, FP32 result) into a
-//      partial that starts from zero every chunk;
-//   3. the partial is promoted into the FP32 accumulator with
-//      acc += partial * (sfa[row] * sfb[col block]) on the vector ALU
-//      (two-level accumulation, section "DeepGEMM" of the same page);
-//   4. after the last chunk the accumulator is rounded to BF16 (nearest even)
+//   1. The A tile (block_m x 128 e4m3), the B tile (block_n x 128 e4m3) and the
+//      block_m A scales of the chunk are copied global -> LDS by direct-to-LDS
+//      loads (global_load_lds_dwordx4), two stages deep: while the chunk in one
+//      stage is multiplied, the next chunk -- of this tile or of the next tile
+//      the workgroup owns -- streams into the other.
+//   2. Each wavefront multiplies its sub-tile with v_mfma_f32_16x16x128_f8f6f4
+//      (OCP e4m3 x e4m3, FP32 result), one instruction per 16x16 output block
+//      per chunk, into a partial that starts from zero every chunk.
+//   3. The partial is promoted into the FP32 accumulator on the vector ALU:
+//      acc += partial * (sfa[row] * sfb[column block]) -- the two-level
+//      accumulation of the same page's "DeepGEMM" section.
+//   4. After the last chunk the accumulator is rounded to BF16 (nearest even)
 //      and stored, only at valid rows and columns.
 //
-// The tile scheduler is persistent: workgroup w processes tiles w, w + grid,
-// ... in a rasterised order (groups of `raster` m-blocks sweep the n-blocks,
-// so concurrently running tiles share B column stripes and A row stripes in
-// L2), and workgroup ids are remapped so that each XCD (workgroups are handed
-// to the 8 XCDs round-robin) runs a contiguous range of that order.
+// MFMA operand roles are transposed: B rows feed the instruction's first
+// operand and A rows its second, so each lane's four results share one A row
+// (one row scale: one multiply per 16x16 block, not four) and cover four
+// consecutive columns (one 8-byte BF16 store).  Lane j of a wavefront supplies
+// TM consecutive A rows across its TM row blocks, so its row scales are one
+// contiguous LDS read.
+//
+// The schedule is persistent: workgroup w processes tiles w, w + grid, ... in
+// a rasterised order (groups of `raster` m-blocks sweep the n-blocks so that
+// concurrent tiles share A and B stripes in L2), with workgroup ids remapped so
+// that each XCD (workgroups are dealt to the 8 XCDs round-robin) runs a
+// contiguous range of that order.
 #include <hip/hip_runtime.h>
 
 #include "fp8bs_internal.h"
@@ -31,37 +41,74 @@ namespace {
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// FP8 (OCP e4m3) x FP8 -> FP32 16x16x128 matrix product with a zero addend.
-// Lane l supplies row (l % 16) of A and column (l % 16) of B, each as 32 bytes
-// of K; the K position of each byte is the same function of (l / 16, byte) for
-// both operands, so any fixed assignment of the chunk's 128 K values to those
-// slots (the same for A and B) yields the full chunk dot product.  Result:
-// lane l holds rows 4 * (l / 16) + v, v = 0..3, of column l % 16.
-__device__ __forceinline__ f32x4 mfma_e4m3_16x16x128(const i32x8& a, const i32x8& b) {
+#define GLOBAL_AS __attribute__((address_space(1)))
+#define LDS_AS __attribute__((address_space(3)))
+
+// 16x16x128 FP8 (OCP e4m3 x e4m3) matrix product with a zero addend.  Lane l
+// supplies row l%16 of the first operand and column l%16 of the second, 32 K
+// bytes each; the K position of each byte is the same function of (l/16, byte)
+// for both operands, so any fixed assignment of the chunk's 128 K values to
+// those slots (identical for both) gives the full chunk dot product.  Lane l
+// receives rows 4*(l/16)+v, v = 0..3, of column l%16.
+__device__ __forceinline__ f32x4 mfma_e4m3(const i32x8& first, const i32x8& second) {
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-    // format codes 0/0 = e4m3 for both operands; no block scaling (scale 0, opsel 0)
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 0, 0, 0);
+    // format codes 0/0 = e4m3 for both operands; block scales off (scale 0, opsel 0)
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(first, second, zero, 0, 0, 0, 0, 0, 0);
 }
 
-__device__ __forceinline__ uint16_t to_bf16_rne(float x) {
-    return __builtin_bit_cast(uint16_t, (__bf16)x);   // v_cvt_pk_bf16_f32, nearest even
+// Wait until this wavefront has no vector-memory operation (direct-to-LDS copies
+// included) and no LDS / scalar-memory operation outstanding.
+__device__ __forceinline__ void wait_loads_all() {
+    // gfx9 s_waitcnt layout: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[15:14]
+    __builtin_amdgcn_s_waitcnt(0x0070);
 }
 
-// Workgroup id -> position in the schedule: workgroup b runs on XCD b % 8, so
-// XCD x is given the contiguous range [x * grid/8, (x+1) * grid/8).
+// Workgroup barrier without a memory fence: the explicit waits before it make this
+// wavefront's copies and reads complete; the clobber keeps the compiler from moving
+// memory accesses across it.
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+__device__ __forceinline__ void dma16(const void* src, LDS_AS void* dst_wave_base) {
+    __builtin_amdgcn_global_load_lds((const GLOBAL_AS void*)src, dst_wave_base, 16, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    const f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));   // v_cvt_pk_bf16_f32
+}
+
+__device__ __forceinline__ uint16_t to_bf16(float x) {
+    return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+// Workgroup id -> position in the schedule.  Workgroup b runs on XCD b % 8, so
+// XCD x is handed the contiguous range [x * grid/8, (x+1) * grid/8).
 __device__ __forceinline__ int logical_block_id() {
     const int n = gridDim.x, b = blockIdx.x;
     if ((n & 7) != 0) return b;
     return (b & 7) * (n >> 3) + (b >> 3);
 }
 
-// Schedule position -> (slot, m-block, n-block).  Masked: slot-major.  Within
-// a slot, groups of `raster` m-blocks sweep all n-blocks column by column.
-template <int LAYOUT>
-__device__ __forceinline__ void map_tile(const GemmParams& p, int t, int& g, int& mb, int& nb) {
-    int rest = t;
-    g = 0;
+// LDS swizzle keys (see the fragment-address comment in the kernel).
+__device__ __forceinline__ int b_key(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+template <int TM>
+__device__ __forceinline__ int a_key(int row) {
+    return TM > 1 ? (row / TM) & 7 : b_key(row);
+}
+
+struct Tile {
+    int g, m0, n0, row_limit;
+};
+
+// Schedule position -> tile.  Masked: slot-major.  Within a slot, groups of
+// `raster` m-blocks sweep the n-blocks column by column.  Returns false when
+// the tile holds no valid row (masked: beyond masked_m; contiguous: padding).
+template <int BM, int BN, int LAYOUT>
+__device__ __forceinline__ bool tile_at(const GemmParams& p, int t, Tile& tl) {
+    int rest = t, g = 0;
     if (LAYOUT == kMasked) {
         const int per_slot = p.m_blocks * p.n_blocks;
         g = t / per_slot;
@@ -72,197 +119,331 @@ __device__ __forceinline__ void map_tile(const GemmParams& p, int t, int& g, int
     const int r = rest - grp * per_group;
     const int first = grp * p.raster;
     const int rows_in = min(p.raster, p.m_blocks - first);
-    mb = first + r % rows_in;
-    nb = r / rows_in;
+    const int mb = first + r % rows_in;
+    const int nb = r / rows_in;
+    tl.m0 = mb * BM;
+    tl.n0 = nb * BN;
+    tl.row_limit = p.m;
+    if (LAYOUT == kMasked) {
+        const int v = min(max(p.masked_m[g], 0), p.m);
+        if (tl.m0 >= v) return false;
+        tl.row_limit = v;
+    } else if (LAYOUT == kContiguous) {
+        const int e = p.grouped_layout[tl.m0];     // a 128-row block: one expert, then padding
+        if (e < 0 || e >= p.num_groups) return false;
+        g = e;
+    }
+    tl.g = g;
+    return true;
+}
+
+template <int BM, int BN, int LAYOUT>
+__device__ __forceinline__ int next_valid_tile(const GemmParams& p, int t, Tile& tl) {
+    for (; t < p.tiles; t += gridDim.x)
+        if (tile_at<BM, BN, LAYOUT>(p, t, tl)) return t;
+    return -1;
 }
 
 template <int BM, int BN, int WM, int WN, int LAYOUT>
 __global__ void __launch_bounds__(64 * WM * WN) fp8bs_gemm_kernel(GemmParams p) {
-    constexpr int NT = 64 * WM * WN;
+    constexpr int NW = WM * WN;                      // wavefronts per workgroup
     constexpr int WTM = BM / WM, WTN = BN / WN;      // wavefront sub-tile
-    constexpr int TM = WTM / 16, TN = WTN / 16;      // 16x16 MFMA tiles per wavefront
+    constexpr int TM = WTM / 16, TN = WTN / 16;      // 16x16 blocks per wavefront
     static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wavefront tile must be a multiple of 16");
-    constexpr int A_BYTES = BM * 128, STAGE = (BM + BN) * 128;
-    constexpr int A_UNITS = BM * 8, B_UNITS = BN * 8;                 // 16-byte units per chunk
-    constexpr int A_PER = (A_UNITS + NT - 1) / NT, B_PER = (B_UNITS + NT - 1) / NT;
+    static_assert(BM % 8 == 0 && BN % 8 == 0 && BM <= 256, "tile shape");
+    static_assert(TM == 1 || TM == 2 || TM == 4 || TM == 8, "row blocks per wavefront");
+    constexpr int A_OFF = 0, B_OFF = BM * 128, SA_OFF = (BM + BN) * 128, SB_OFF = SA_OFF + BM * 4;
+    constexpr int STAGE = stage_bytes(BM, BN);
+    constexpr int A_INS = BM / 8, B_INS = BN / 8;    // 1 KB (8 rows) per wavefront copy
+    constexpr int A_PER = (A_INS + NW - 1) / NW, B_PER = (B_INS + NW - 1) / NW;
+    constexpr int SB_SPAN = BN / 128 + 2;            // B-scale blocks a tile can touch
+    // the wave's columns lie in one 128-column scale block for every tile
+    constexpr bool UNIFORM_SB = (BN % 128 == 0) && (128 % WTN == 0);
 
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * STAGE];
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave / WN, wn = wave % WN;
     const int kchunks = p.k / 128;
-    const int64_t K = p.k;
-    const int nsb = (p.n + 127) / 128;               // B scale blocks along N
+    const int K = p.k;
+    const int nsb = (p.n + 127) / 128;
 
-    for (int t = logical_block_id(); t < p.tiles; t += gridDim.x) {
-        int g, mb, nb;
-        map_tile<LAYOUT>(p, t, g, mb, nb);
-        const int m0 = mb * BM, n0 = nb * BN;
-        int row_limit = p.m;                         // rows of this slot that exist/are valid
-        if (LAYOUT == kMasked) {
-            const int v = min(max(p.masked_m[g], 0), p.m);
-            if (m0 >= v) continue;                   // nothing valid in this tile
-            row_limit = v;
-        } else if (LAYOUT == kContiguous) {
-            const int e = p.grouped_layout[m0];      // a block holds one expert, then padding
-            if (e < 0 || e >= p.num_groups) continue;
-            g = e;
+    // ---- fragment read addresses (byte offsets in a stage) ----
+    // Rows are 128 bytes; 16-byte unit u of row r is stored at slot u ^ key(r).  A read of
+    // 16 bytes per lane is free of bank conflicts when lanes 0-7 (and 8-15) hit eight
+    // distinct slots and lanes 0-15 hit sixteen distinct (row parity, slot) pairs.
+    // A rows (TM > 1): lane j = l%16 owns rows wm*WTM + TM*j + (i ^ flip), flip = j / 8
+    // (rows of lanes j and j+8 differ in parity), key = (row / TM) & 7 = j & 7.
+    // B rows (and A rows when TM == 1): lane i' reads row base + i', key = (i' & 7) ^ (i' / 8).
+    // Neither key depends on the block index, so block i / j is an immediate offset.
+    const int lj = lane & 15;
+    const int kq = lane >> 4;                         // 32-byte quarter of the chunk
+    const int flip = (TM > 1) ? (lj >> 3) : 0;
+    int a_even[2], a_odd[2];                          // row block i at +128*i (even / odd i)
+    {
+        const int row0 = wm * WTM + TM * lj;
+        const int key = a_key<TM>(row0);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int base = A_OFF + row0 * 128 + (((2 * kq + h) ^ key) << 4);
+            a_even[h] = base + flip * 128;            // (i ^ flip) = i + flip for even i
+            a_odd[h] = base - flip * 128;             // (i ^ flip) = i - flip for odd i
         }
+    }
+    int b_base[2];                                    // column block j at +2048*j
+    {
+        const int row0 = wn * WTN + lj;
+        const int key = b_key(row0);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) b_base[h] = B_OFF + row0 * 128 + (((2 * kq + h) ^ key) << 4);
+    }
+    const int sa_rd = SA_OFF + (wm * WTM + TM * lj) * 4;
 
-        const uint8_t* a_g = p.a + (LAYOUT == kMasked ? (int64_t)g * p.m * K : (int64_t)0);
-        const uint8_t* b_g = p.b + (int64_t)g * p.n * K;
-        const float* sfa_g = p.sfa + (LAYOUT == kMasked ? (int64_t)g * kchunks * p.sfa_ld : (int64_t)0);
-        const float* sfb_g = p.sfb + (int64_t)g * nsb * kchunks;
+    // ---- copies: wavefront copy `ins` moves tile rows 8*ins .. 8*ins+7; lane L fills LDS
+    // slot L%8 of row 8*ins + L/8 with the global 16-byte unit (slot ^ key(row)) ----
+    const int cp_row = lane >> 3, cp_slot = lane & 7;
+    int sb_blk0 = 0;                                  // first B-scale block of the issue tile
+    auto prepare = [&](const Tile& tl) { sb_blk0 = tl.n0 / 128; };
 
-        // ---- per-thread global->LDS copy assignment (16 bytes per unit) ----
-        int64_t a_src[A_PER];
-        int a_dst[A_PER];
-        bool a_ok[A_PER];
+    // copy chunk c of tile `tl` into stage s (per-lane offsets recomputed: registers are
+    // scarcer than the few address instructions)
+    auto issue = [&](const Tile& tl, int c, int s) {
+        uint8_t* st = smem + s * STAGE;
+        const uint8_t* a_base = p.a + (LAYOUT == kMasked ? (int64_t)tl.g * p.m * K : (int64_t)0) +
+                                (int64_t)c * 128;
+        const uint8_t* b_base = p.b + (int64_t)tl.g * p.n * K + (int64_t)c * 128;
 #pragma unroll
-        for (int i = 0; i < A_PER; ++i) {
-            const int u = tid + i * NT;
-            const int row = u >> 3, q = u & 7;
-            a_ok[i] = (A_UNITS % NT == 0) || u < A_UNITS;
-            const int grow = min(m0 + row, row_limit - 1);      // clamp: never read past the slot
-            a_src[i] = (int64_t)grow * K + q * 16;
-            a_dst[i] = row * 128 + ((q ^ (row & 7)) << 4);
-        }
-        int64_t b_src[B_PER];
-        int b_dst[B_PER];
-        bool b_ok[B_PER];
-#pragma unroll
-        for (int i = 0; i < B_PER; ++i) {
-            const int u = tid + i * NT;
-            const int row = u >> 3, q = u & 7;
-            b_ok[i] = (B_UNITS % NT == 0) || u < B_UNITS;
-            const int grow = min(n0 + row, p.n - 1);
-            b_src[i] = (int64_t)grow * K + q * 16;
-            b_dst[i] = A_BYTES + row * 128 + ((q ^ (row & 7)) << 4);
-        }
-
-        // ---- per-lane fragment addresses in a stage ----
-        const int kg = lane >> 4;                     // which 32-byte quarter of the chunk
-        int a_frag[TM][2], b_frag[TN][2];
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            const int row = wm * WTM + i * 16 + (lane & 15);
-#pragma unroll
-            for (int h = 0; h < 2; ++h) a_frag[i][h] = row * 128 + (((2 * kg + h) ^ (row & 7)) << 4);
-        }
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int row = wn * WTN + j * 16 + (lane & 15);
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-                b_frag[j][h] = A_BYTES + row * 128 + (((2 * kg + h) ^ (row & 7)) << 4);
-        }
-        // rows of the four accumulator values this lane holds in sub-tile i
-        int sa_row[TM];
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            const int r4 = m0 + wm * WTM + i * 16 + kg * 4;
-            sa_row[i] = r4 < p.sfa_ld ? r4 : 0;       // groups of 4 rows lie wholly inside or outside
-        }
-        int sb_blk[TN];
-#pragma unroll
-        for (int j = 0; j < TN; ++j) sb_blk[j] = min(n0 + wn * WTN + j * 16, p.n - 1) / 128;
-
-        f32x4 acc[TM][TN];
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-        i32x4 ra[A_PER], rb[B_PER];
-        // prologue: chunk 0 -> stage 0
-#pragma unroll
-        for (int i = 0; i < A_PER; ++i)
-            if (a_ok[i]) ra[i] = *(const i32x4*)(a_g + a_src[i]);
-#pragma unroll
-        for (int i = 0; i < B_PER; ++i)
-            if (b_ok[i]) rb[i] = *(const i32x4*)(b_g + b_src[i]);
-#pragma unroll
-        for (int i = 0; i < A_PER; ++i)
-            if (a_ok[i]) *(i32x4*)(smem + a_dst[i]) = ra[i];
-#pragma unroll
-        for (int i = 0; i < B_PER; ++i)
-            if (b_ok[i]) *(i32x4*)(smem + b_dst[i]) = rb[i];
-        __syncthreads();
-
-        for (int c = 0; c < kchunks; ++c) {
-            const bool more = c + 1 < kchunks;
-            if (more) {
-                const int64_t off = (int64_t)(c + 1) * 128;
-#pragma unroll
-                for (int i = 0; i < A_PER; ++i)
-                    if (a_ok[i]) ra[i] = *(const i32x4*)(a_g + a_src[i] + off);
-#pragma unroll
-                for (int i = 0; i < B_PER; ++i)
-                    if (b_ok[i]) rb[i] = *(const i32x4*)(b_g + b_src[i] + off);
+        for (int k = 0; k < A_PER; ++k) {
+            const int ins = wave + k * NW;
+            if (A_INS % NW == 0 || ins < A_INS) {
+                const int row = 8 * ins + cp_row;
+                const int grow = min(tl.m0 + row, tl.row_limit - 1);
+                const uint32_t off = (uint32_t)grow * (uint32_t)K + (uint32_t)((cp_slot ^ a_key<TM>(row)) << 4);
+                dma16(a_base + off, (LDS_AS void*)(st + A_OFF + ins * 1024));
             }
-            // scales of chunk c
-            f32x4 sa[TM];
+        }
 #pragma unroll
-            for (int i = 0; i < TM; ++i) sa[i] = *(const f32x4*)(sfa_g + (int64_t)c * p.sfa_ld + sa_row[i]);
-            float sb[TN];
-#pragma unroll
-            for (int j = 0; j < TN; ++j) sb[j] = sfb_g[sb_blk[j] * kchunks + c];
+        for (int k = 0; k < B_PER; ++k) {
+            const int ins = wave + k * NW;
+            if (B_INS % NW == 0 || ins < B_INS) {
+                const int row = 8 * ins + cp_row;
+                const int grow = min(tl.n0 + row, p.n - 1);
+                const uint32_t off = (uint32_t)grow * (uint32_t)K + (uint32_t)((cp_slot ^ b_key(row)) << 4);
+                dma16(b_base + off, (LDS_AS void*)(st + B_OFF + ins * 1024));
+            }
+        }
+        if (wave == NW - 1) {
+            // the chunk's block_m A scales (MN-major: contiguous) and the B-scale values of
+            // the column blocks the tile touches
+            const uint8_t* sa_base = (const uint8_t*)(p.sfa +
+                (LAYOUT == kMasked ? (int64_t)tl.g * kchunks * p.sfa_ld : (int64_t)0) +
+                (int64_t)c * p.sfa_ld);
+            int r4 = tl.m0 + 4 * lane;                // rows past the scale array are unused
+            if (r4 >= p.sfa_ld) r4 = 0;
+            if (4 * lane < BM) dma16(sa_base + (uint32_t)r4 * 4u, (LDS_AS void*)(st + SA_OFF));
+            const uint8_t* sb_base = (const uint8_t*)(p.sfb + (int64_t)tl.g * nsb * kchunks + c);
+            const uint32_t sb_off = (uint32_t)min(tl.n0 / 128 + lane, nsb - 1) * (uint32_t)kchunks * 4u;
+            if (lane < SB_SPAN)
+                __builtin_amdgcn_global_load_lds((const GLOBAL_AS void*)(sb_base + sb_off),
+                                                 (LDS_AS void*)(st + SB_OFF), 4, 0, 0);
+        }
+    };
 
-            const uint8_t* st = smem + (c & 1) * STAGE;
-            i32x8 af[TM], bf[TN];
+    // ---- LDS fragment and scale readers (stage base `st`) ----
+    auto load_a = [&](const uint8_t* st, int i) {
+        const int* base = (i & 1) ? a_odd : a_even;
+        const i32x4 lo = *(const i32x4*)(st + base[0] + 128 * i);
+        const i32x4 hi = *(const i32x4*)(st + base[1] + 128 * i);
+        return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+    auto load_b = [&](const uint8_t* st, int j) {
+        const i32x4 lo = *(const i32x4*)(st + b_base[0] + 2048 * j);
+        const i32x4 hi = *(const i32x4*)(st + b_base[1] + 2048 * j);
+        return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+    // The operand with fewer 16-row blocks stays in registers for the whole chunk; the
+    // other is streamed block by block (double buffered).
+    constexpr bool STREAM_A = TM >= TN;
+    constexpr int NO = STREAM_A ? TM : TN;             // streamed blocks
+    constexpr int NI = STREAM_A ? TN : TM;             // resident blocks
+
+    // registers holding one chunk's operands: resident fragments, the first streamed
+    // fragment, and the promotion scales sc[i][j] = sfa(row block i) * sfb(column block j)
+    struct ChunkRegs {
+        i32x8 res[NI];
+        i32x8 first;
+    };
+    struct ScaleRegs {
+        float sa[TM];
+        float sb[UNIFORM_SB ? 1 : TN];
+    };
+    auto load_scales = [&](const uint8_t* st, const Tile& tl, int blk0, ScaleRegs& r) {
+        const float* sap = (const float*)(st + sa_rd);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) r.sa[i] = sap[i];
+        if (TM > 1) {
+#pragma unroll
+            for (int i = 0; i < TM; i += 2) {             // this lane's rows are i ^ flip
+                const float x = r.sa[i], y = r.sa[i + 1];
+                r.sa[i] = flip ? y : x;
+                r.sa[i + 1] = flip ? x : y;
+            }
+        }
+        const float* sbl = (const float*)(st + SB_OFF);
+        if (UNIFORM_SB) {
+            r.sb[0] = sbl[min(tl.n0 + wn * WTN, p.n - 1) / 128 - blk0];
+        } else {
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                r.sb[j] = sbl[min(tl.n0 + wn * WTN + 16 * j, p.n - 1) / 128 - blk0];
+        }
+    };
+
+    Tile cur;
+    int t = next_valid_tile<BM, BN, LAYOUT>(p, logical_block_id(), cur);
+    if (t < 0) return;
+
+    f32x4 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    prepare(cur);
+    issue(cur, 0, 0);
+    int cur_sb_blk0 = sb_blk0;
+    wait_loads_all();
+    block_barrier();                                   // chunk 0 of the first tile is in stage 0
+    ChunkRegs cr;
+#pragma unroll
+    for (int q = 0; q < NI; ++q) cr.res[q] = STREAM_A ? load_b(smem, q) : load_a(smem, q);
+    cr.first = STREAM_A ? load_a(smem, 0) : load_b(smem, 0);
+
+    int c = 0, s = 0;
+    for (;;) {
+        // Invariant: chunk c of tile `cur` is in stage s and its resident fragments, first
+        // streamed fragment and scales are loaded (or in flight) in `cr`; every wavefront
+        // has finished reading stage s^1.
+        const bool last = c + 1 == kchunks;
+        // contiguous layout: which of this lane's rows belong to the tile's expert
+        uint32_t row_ok_bits = 0;
+        if (last) {
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
-                const i32x4 lo = *(const i32x4*)(st + a_frag[i][0]);
-                const i32x4 hi = *(const i32x4*)(st + a_frag[i][1]);
-                af[i] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                const int row = cur.m0 + wm * WTM + TM * lj + (i ^ flip);
+                bool ok = row < cur.row_limit;
+                if (LAYOUT == kContiguous && ok) ok = p.grouped_layout[row] == cur.g;
+                row_ok_bits |= (ok ? 1u : 0u) << i;
             }
+        }
+        Tile nxt = cur;
+        int nt = t, nc = c + 1;
+        bool have_next = true;
+        if (last) {
+            nc = 0;
+            nt = next_valid_tile<BM, BN, LAYOUT>(p, t + gridDim.x, nxt);
+            have_next = nt >= 0;
+            if (have_next) prepare(nxt);
+        }
+        if (have_next) issue(nxt, nc, s ^ 1);
+
+        const uint8_t* st = smem + s * STAGE;
+        float sc[TM][UNIFORM_SB ? 1 : TN];
+        {
+            ScaleRegs sr;
+            load_scales(st, cur, cur_sb_blk0, sr);
 #pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const i32x4 lo = *(const i32x4*)(st + b_frag[j][0]);
-                const i32x4 hi = *(const i32x4*)(st + b_frag[j][1]);
-                bf[j] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            }
+            for (int i = 0; i < TM; ++i)
 #pragma unroll
-            for (int i = 0; i < TM; ++i) {
+                for (int j = 0; j < (UNIFORM_SB ? 1 : TN); ++j) sc[i][j] = sr.sa[i] * sr.sb[j];
+        }
+        auto promote = [&](int o, int q, const f32x4& part) {
+            const int i = STREAM_A ? o : q, j = STREAM_A ? q : o;
+            acc[i][j] += part * sc[i][UNIFORM_SB ? 0 : j];
+        };
+        // Products are issued in the order (o, q), o = streamed block, q = resident block;
+        // the result of product k is promoted after product k+LAG has issued, so its
+        // latency is covered and only LAG+1 partials are live.
+        constexpr int LAG = 2;
+        f32x4 ring[LAG + 1];
+        auto step = [&](int o, int q, const i32x8& fr, const i32x8* res) {
+            const int k = o * NI + q;
+            ring[k % (LAG + 1)] = STREAM_A ? mfma_e4m3(res[q], fr) : mfma_e4m3(fr, res[q]);
+            if (k >= LAG) promote((k - LAG) / NI, (k - LAG) % NI, ring[(k - LAG) % (LAG + 1)]);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // the MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);       // the promotion it covers
+        };
+
+        // ---- streamed blocks 0 .. NO-2 ----
+        i32x8 fr = cr.first;
 #pragma unroll
-                for (int j = 0; j < TN; ++j) {
-                    const f32x4 part = mfma_e4m3_16x16x128(af[i], bf[j]);
+        for (int o = 0; o + 1 < NO; ++o) {
+            const i32x8 next_fr = STREAM_A ? load_a(st, o + 1) : load_b(st, o + 1);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);       // next fragment reads
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) acc[i][j][v] += part[v] * (sa[i][v] * sb[j]);
-                }
-            }
-            if (more) {
-                uint8_t* nx = smem + ((c + 1) & 1) * STAGE;
-#pragma unroll
-                for (int i = 0; i < A_PER; ++i)
-                    if (a_ok[i]) *(i32x4*)(nx + a_dst[i]) = ra[i];
-#pragma unroll
-                for (int i = 0; i < B_PER; ++i)
-                    if (b_ok[i]) *(i32x4*)(nx + b_dst[i]) = rb[i];
-            }
-            __syncthreads();
+            for (int q = 0; q < NI; ++q) step(o, q, fr, cr.res);
+            fr = next_fr;
         }
 
-        // ---- epilogue: BF16 stores at valid rows / columns only ----
-        uint16_t* d_g = p.d + (LAYOUT == kMasked ? (int64_t)g * p.m * p.n : (int64_t)0);
+        // ---- last block: every read of stage s has been issued.  Wait for them and for
+        // this wavefront's copies of the next chunk, meet the other wavefronts, then start
+        // reading the next chunk while the last products of this chunk issue ----
+        // (Branch free: after the last chunk the barrier and the reads are harmless, and one
+        // basic block lets the scheduler interleave the whole chunk.)
+        wait_loads_all();
+        block_barrier();
+        ChunkRegs nr;
+        {
+            const uint8_t* nst = smem + (s ^ 1) * STAGE;
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
+            for (int q = 0; q < NI; ++q) {
+                step(NO - 1, q, fr, cr.res);   // frees resident fragment q ...
+                nr.res[q] = STREAM_A ? load_b(nst, q) : load_a(nst, q);   // ... for this
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            nr.first = STREAM_A ? load_a(nst, 0) : load_b(nst, 0);
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int row = m0 + wm * WTM + i * 16 + kg * 4 + v;
-                bool row_ok = row < row_limit;
-                if (LAYOUT == kContiguous && row_ok) row_ok = p.grouped_layout[row] == g;
-                if (!row_ok) continue;
-                uint16_t* drow = d_g + (int64_t)row * p.n;
+            for (int k = NO * NI - LAG; k < NO * NI; ++k)
+                if (k >= 0) promote(k / NI, k % NI, ring[k % (LAG + 1)]);
+        }
+
+        if (last) {
+            // ---- epilogue: BF16 at valid rows / columns only ----
+            uint16_t* d_g = p.d + (LAYOUT == kMasked ? (int64_t)cur.g * p.m * p.n : (int64_t)0);
+            const bool vec_ok = (p.n & 3) == 0;
 #pragma unroll
-                for (int j = 0; j < TN; ++j) {
-                    const int col = n0 + wn * WTN + j * 16 + (lane & 15);
-                    if (col < p.n) drow[col] = to_bf16_rne(acc[i][j][v]);
+            for (int i = 0; i < TM; ++i) {
+                if (row_ok_bits & (1u << i)) {
+                    const int row = cur.m0 + wm * WTM + TM * lj + (i ^ flip);
+                    uint16_t* drow = d_g + (int64_t)row * p.n;
+#pragma unroll
+                    for (int j = 0; j < TN; ++j) {
+                        const int col = cur.n0 + wn * WTN + 16 * j + 4 * kq;
+                        const f32x4 v = acc[i][j];
+                        if (vec_ok && col + 3 < p.n) {
+                            uint2 w;
+                            w.x = pack_bf16x2(v[0], v[1]);
+                            w.y = pack_bf16x2(v[2], v[3]);
+                            *(uint2*)(drow + col) = w;
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                if (col + e < p.n) drow[col + e] = to_bf16(v[e]);
+                        }
+                    }
                 }
+#pragma unroll
+                for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
         }
+        if (!have_next) break;
+        if (last) cur_sb_blk0 = sb_blk0;
+        t = nt;
+        cur = nxt;
+        c = nc;
+        s ^= 1;
+        cr = nr;
     }
 }
 
@@ -273,7 +454,7 @@ struct InstanceEntry {
     int threads;
 };
 
-#define FP8BS_INSTANCE(BM, BN, WM, WN, OCC)                                   \
+#define FP8BS_INSTANCE(BM, BN, WM, WN, OCC, EFF)                              \
     {{fp8bs_gemm_kernel<BM, BN, WM, WN, kDense>,                              \
       fp8bs_gemm_kernel<BM, BN, WM, WN, kContiguous>,                         \
       fp8bs_gemm_kernel<BM, BN, WM, WN, kMasked>},                            \

@@ -3,7 +3,7 @@
 #pragma once
 #include <stdint.h>
 
-#include "../../include/fp8bs.h"
+#include "fp8bs.h"
 
 namespace fp8bs {
 
@@ -16,7 +16,15 @@ struct InstanceShape {
     int block_m, block_n, waves_m, waves_n;
     int wg_per_cu;       // workgroups per CU the launch assumes (LDS / register bound)
     int lds_bytes;
+    int eff_pct;         // cost-model credit: percent of the MFMA peak when compute bound
 };
+
+// LDS bytes of one pipeline stage: the A tile, the B tile (128 K bytes per
+// row), the tile's block_m A scales and up to 64 B-scale values.
+constexpr int stage_bytes(int block_m, int block_n) {
+    return (block_m + block_n) * 128 + block_m * 4 + 256;
+}
+constexpr int kStages = 2;
 
 // The instance table (defined next to the kernels, read by the planner).
 extern const InstanceShape kInstances[];

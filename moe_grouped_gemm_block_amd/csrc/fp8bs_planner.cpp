@@ -16,7 +16,8 @@
 
 namespace fp8bs {
 
-#define FP8BS_INSTANCE(BM, BN, WM, WN, OCC) {BM, BN, WM, WN, OCC, 2 * ((BM) + (BN)) * 128},
+#define FP8BS_INSTANCE(BM, BN, WM, WN, OCC, EFF) \
+    {BM, BN, WM, WN, OCC, kStages * stage_bytes(BM, BN), EFF},
 const InstanceShape kInstances[] = {
 #include "fp8bs_instances.inc"
 };
@@ -30,6 +31,8 @@ int validate_sizes(int layout, int64_t m, int n, int k, int num_groups) {
     if (layout != kDense && num_groups < 1) return FP8BS_ERR_SHAPE;
     if (layout == kDense && num_groups != 1) return FP8BS_ERR_SHAPE;
     if (m > (int64_t)0x7fffffff) return FP8BS_ERR_SHAPE;
+    // copies address one A slot (m x k bytes) and one B group (n x k bytes) with 32-bit offsets
+    if ((double)m * k >= 4294967296.0 || (double)n * k >= 4294967296.0) return FP8BS_ERR_SHAPE;
     // element offsets are 64-bit in the kernels; keep every operand below 2^62 bytes
     const double rows = (double)m * (layout == kMasked ? num_groups : 1);
     if (rows * k > 4.0e18 || rows * n * 2.0 > 4.0e18 || (double)num_groups * n * k > 4.0e18)
@@ -37,11 +40,29 @@ int validate_sizes(int layout, int64_t m, int n, int k, int num_groups) {
     return FP8BS_OK;
 }
 
-// Cost model constants (per CU, per clock): FP8 MFMA issue rate and the
-// operand bandwidth a CU can draw from L2.  Only the ranking matters.
+// Cost model (cycles of one CU).  A tile costs the largest of its MFMA time at
+// the instance's credited efficiency, its LDS traffic (fragment reads by every
+// wavefront plus the copies in) and its operand traffic from L2; a CU works
+// through ceil(tiles / CUs) tiles; the whole chip cannot beat reading every
+// operand byte once from HBM.
 static const double kMfmaFlopPerClk = 8192.0;
+static const double kLdsBytesPerClk = 160.0;
 static const double kL2BytesPerClk = 64.0;
 static const double kHbmBytesPerClk = 8.0e12 / 2.4e9;   // whole chip
+
+static double tile_cycles(const InstanceShape& s, int k) {
+    const int nw = s.waves_m * s.waves_n;
+    const double wtm = s.block_m / s.waves_m, wtn = s.block_n / s.waves_n;
+    const double chunks = k / 128.0;
+    const double t_mfma = 2.0 * s.block_m * s.block_n * (double)k / (kMfmaFlopPerClk * s.eff_pct / 100.0);
+    const double t_lds = chunks * (nw * (wtm + wtn) * 128.0 + (s.block_m + s.block_n) * 128.0) /
+                         kLdsBytesPerClk;
+    const double t_feed = (double)(s.block_m + s.block_n) * k / kL2BytesPerClk;
+    double t = t_mfma;
+    if (t_lds > t) t = t_lds;
+    if (t_feed > t) t = t_feed;
+    return t;
+}
 
 static void fill_launch(int i, int layout, int64_t m, int n, int num_groups, int num_cus,
                         Plan* out) {
@@ -92,17 +113,14 @@ int plan_request(int layout, int64_t m, int n, int k, int num_groups, int expect
         if (tiles > 0x7fffffff) continue;
         const int64_t eff_m_blocks = (eff_rows + s.block_m - 1) / s.block_m;
         const int64_t eff_tiles = (layout == kMasked ? G : 1) * eff_m_blocks * n_blocks;
-        const int64_t slots = (int64_t)num_cus * s.wg_per_cu;
-        const int64_t waves = eff_tiles == 0 ? 0 : (eff_tiles + slots - 1) / slots;
-        // one tile on one CU shared with wg_per_cu - 1 others
-        const double t_mfma = 2.0 * s.block_m * s.block_n * (double)k / kMfmaFlopPerClk;
-        const double t_feed = (double)(s.block_m + s.block_n) * k / kL2BytesPerClk;
-        const double t_tile = (t_mfma > t_feed ? t_mfma : t_feed) * s.wg_per_cu;
-        // whole-chip HBM floor: every operand byte at least once
+        const int64_t per_cu = (eff_tiles + num_cus - 1) / num_cus;
         const double bytes = (double)G * eff_rows * k + (double)G * n * k + (double)G * eff_rows * n * 2;
         const double t_hbm = bytes / kHbmBytesPerClk;
-        double t = waves * t_tile;
+        double t = per_cu * tile_cycles(s, k);
         if (t < t_hbm) t = t_hbm;
+        // fewer busy CUs also means fewer loads in flight: penalise under-fill
+        const double fill = (double)(eff_tiles < num_cus ? eff_tiles : num_cus) / num_cus;
+        t *= 1.0 + 0.1 * (1.0 - fill);
         if (best < 0 || t < best_t * (1.0 - 1e-9)) {
             best = i;
             best_t = t;
