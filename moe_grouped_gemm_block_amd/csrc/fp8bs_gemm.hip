@@ -208,29 +208,56 @@ __global__ void __launch_bounds__(64 * WM * WN) fp8bs_gemm_kernel(GemmParams p) 
 
     // copy chunk c of tile `tl` into stage s (per-lane offsets recomputed: registers are
     // scarcer than the few address instructions)
+    // The swizzle key of a copied row is the same for rows r and r + 8*NW, so the lane
+    // offset of every copy of a tile is one value plus a uniform multiple of 8*NW rows.
+    static_assert((TM == 1 || NW % TM == 0) && NW % 2 == 0, "copy offsets must repeat");
+    const uint32_t a_lane = (uint32_t)(8 * wave + cp_row) * (uint32_t)K +
+                            (uint32_t)((cp_slot ^ a_key<TM>(8 * wave + cp_row)) << 4);
+    const uint32_t b_lane = (uint32_t)(8 * wave + cp_row) * (uint32_t)K +
+                            (uint32_t)((cp_slot ^ b_key(8 * wave + cp_row)) << 4);
     auto issue = [&](const Tile& tl, int c, int s) {
         uint8_t* st = smem + s * STAGE;
         const uint8_t* a_base = p.a + (LAYOUT == kMasked ? (int64_t)tl.g * p.m * K : (int64_t)0) +
                                 (int64_t)c * 128;
         const uint8_t* b_base = p.b + (int64_t)tl.g * p.n * K + (int64_t)c * 128;
+        if (tl.m0 + BM <= tl.row_limit) {             // whole tile inside: no clamping
+            const uint8_t* a_t = a_base + (int64_t)tl.m0 * K;
 #pragma unroll
-        for (int k = 0; k < A_PER; ++k) {
-            const int ins = wave + k * NW;
-            if (A_INS % NW == 0 || ins < A_INS) {
-                const int row = 8 * ins + cp_row;
-                const int grow = min(tl.m0 + row, tl.row_limit - 1);
-                const uint32_t off = (uint32_t)grow * (uint32_t)K + (uint32_t)((cp_slot ^ a_key<TM>(row)) << 4);
-                dma16(a_base + off, (LDS_AS void*)(st + A_OFF + ins * 1024));
+            for (int k = 0; k < A_PER; ++k) {
+                const int ins = wave + k * NW;
+                if (A_INS % NW == 0 || ins < A_INS)
+                    dma16(a_t + (int64_t)k * 8 * NW * K + a_lane, (LDS_AS void*)(st + A_OFF + ins * 1024));
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < A_PER; ++k) {
+                const int ins = wave + k * NW;
+                if (A_INS % NW == 0 || ins < A_INS) {
+                    const int row = 8 * ins + cp_row;
+                    const int grow = min(tl.m0 + row, tl.row_limit - 1);
+                    const uint32_t off = (uint32_t)grow * (uint32_t)K + (uint32_t)((cp_slot ^ a_key<TM>(row)) << 4);
+                    dma16(a_base + off, (LDS_AS void*)(st + A_OFF + ins * 1024));
+                }
             }
         }
+        if (tl.n0 + BN <= p.n) {
+            const uint8_t* b_t = b_base + (int64_t)tl.n0 * K;
 #pragma unroll
-        for (int k = 0; k < B_PER; ++k) {
-            const int ins = wave + k * NW;
-            if (B_INS % NW == 0 || ins < B_INS) {
-                const int row = 8 * ins + cp_row;
-                const int grow = min(tl.n0 + row, p.n - 1);
-                const uint32_t off = (uint32_t)grow * (uint32_t)K + (uint32_t)((cp_slot ^ b_key(row)) << 4);
-                dma16(b_base + off, (LDS_AS void*)(st + B_OFF + ins * 1024));
+            for (int k = 0; k < B_PER; ++k) {
+                const int ins = wave + k * NW;
+                if (B_INS % NW == 0 || ins < B_INS)
+                    dma16(b_t + (int64_t)k * 8 * NW * K + b_lane, (LDS_AS void*)(st + B_OFF + ins * 1024));
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < B_PER; ++k) {
+                const int ins = wave + k * NW;
+                if (B_INS % NW == 0 || ins < B_INS) {
+                    const int row = 8 * ins + cp_row;
+                    const int grow = min(tl.n0 + row, p.n - 1);
+                    const uint32_t off = (uint32_t)grow * (uint32_t)K + (uint32_t)((cp_slot ^ b_key(row)) << 4);
+                    dma16(b_base + off, (LDS_AS void*)(st + B_OFF + ins * 1024));
+                }
             }
         }
         if (wave == NW - 1) {
@@ -369,7 +396,9 @@ __global__ void __launch_bounds__(64 * WM * WN) fp8bs_gemm_kernel(GemmParams p) 
         f32x4 ring[LAG + 1];
         auto step = [&](int o, int q, const i32x8& fr, const i32x8* res) {
             const int k = o * NI + q;
+            __builtin_amdgcn_s_setprio(1);             // favour the wave that feeds the MFMA pipe
             ring[k % (LAG + 1)] = STREAM_A ? mfma_e4m3(res[q], fr) : mfma_e4m3(fr, res[q]);
+            __builtin_amdgcn_s_setprio(0);
             if (k >= LAG) promote((k - LAG) / NI, (k - LAG) % NI, ring[(k - LAG) % (LAG + 1)]);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // the MFMA
             __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);       // the promotion it covers
@@ -454,7 +483,7 @@ struct InstanceEntry {
     int threads;
 };
 
-#define FP8BS_INSTANCE(BM, BN, WM, WN, OCC, EFF)                              \
+#define FP8BS_INSTANCE(BM, BN, WM, WN, OCC, CNS, TNS)                         \
     {{fp8bs_gemm_kernel<BM, BN, WM, WN, kDense>,                              \
       fp8bs_gemm_kernel<BM, BN, WM, WN, kContiguous>,                         \
       fp8bs_gemm_kernel<BM, BN, WM, WN, kMasked>},                            \

@@ -16,7 +16,8 @@ struct InstanceShape {
     int block_m, block_n, waves_m, waves_n;
     int wg_per_cu;       // workgroups per CU the launch assumes (LDS / register bound)
     int lds_bytes;
-    int eff_pct;         // cost-model credit: percent of the MFMA peak when compute bound
+    int chunk_ns;        // cost model: CU time per 128-K chunk of one tile
+    int tile_ns;         // cost model: CU time per tile (prologue / epilogue)
 };
 
 // LDS bytes of one pipeline stage: the A tile, the B tile (128 K bytes per

@@ -16,8 +16,8 @@
 
 namespace fp8bs {
 
-#define FP8BS_INSTANCE(BM, BN, WM, WN, OCC, EFF) \
-    {BM, BN, WM, WN, OCC, kStages * stage_bytes(BM, BN), EFF},
+#define FP8BS_INSTANCE(BM, BN, WM, WN, OCC, CNS, TNS) \
+    {BM, BN, WM, WN, OCC, kStages * stage_bytes(BM, BN), CNS, TNS},
 const InstanceShape kInstances[] = {
 #include "fp8bs_instances.inc"
 };
@@ -40,29 +40,11 @@ int validate_sizes(int layout, int64_t m, int n, int k, int num_groups) {
     return FP8BS_OK;
 }
 
-// Cost model (cycles of one CU).  A tile costs the largest of its MFMA time at
-// the instance's credited efficiency, its LDS traffic (fragment reads by every
-// wavefront plus the copies in) and its operand traffic from L2; a CU works
-// through ceil(tiles / CUs) tiles; the whole chip cannot beat reading every
-// operand byte once from HBM.
-static const double kMfmaFlopPerClk = 8192.0;
-static const double kLdsBytesPerClk = 160.0;
-static const double kL2BytesPerClk = 64.0;
-static const double kHbmBytesPerClk = 8.0e12 / 2.4e9;   // whole chip
-
-static double tile_cycles(const InstanceShape& s, int k) {
-    const int nw = s.waves_m * s.waves_n;
-    const double wtm = s.block_m / s.waves_m, wtn = s.block_n / s.waves_n;
-    const double chunks = k / 128.0;
-    const double t_mfma = 2.0 * s.block_m * s.block_n * (double)k / (kMfmaFlopPerClk * s.eff_pct / 100.0);
-    const double t_lds = chunks * (nw * (wtm + wtn) * 128.0 + (s.block_m + s.block_n) * 128.0) /
-                         kLdsBytesPerClk;
-    const double t_feed = (double)(s.block_m + s.block_n) * k / kL2BytesPerClk;
-    double t = t_mfma;
-    if (t_lds > t) t = t_lds;
-    if (t_feed > t) t = t_feed;
-    return t;
-}
+// Cost model (nanoseconds).  A CU works through ceil(tiles / CUs) tiles, each costing
+// chunks * chunk_ns + tile_ns (measured per instance); the whole chip cannot beat
+// reading every operand byte once from HBM; and a launch that leaves CUs idle keeps
+// fewer loads in flight, so under-fill is penalised.
+static const double kHbmBytesPerNs = 8.0e12 / 1.0e9;
 
 static void fill_launch(int i, int layout, int64_t m, int n, int num_groups, int num_cus,
                         Plan* out) {
@@ -101,6 +83,11 @@ int plan_request(int layout, int64_t m, int n, int k, int num_groups, int expect
     const int G = layout == kDense ? 1 : num_groups;
     int64_t eff_rows = m;                        // rows per group the estimate assumes
     if (layout == kMasked && expected_m > 0 && expected_m < m) eff_rows = expected_m;
+    // masked: expected_m is read as the mean of masked_m, spread uniformly over
+    // 1 .. min(2 * expected_m, max_m); a group costs E[ceil(masked_m / block_m)] m-blocks
+    const int64_t spread = layout == kMasked && expected_m > 0
+                               ? (2 * (int64_t)expected_m < m ? 2 * (int64_t)expected_m : m)
+                               : 0;
     double best_t = 0;
     int best = -1;
     Plan best_plan = {};
@@ -111,14 +98,22 @@ int plan_request(int layout, int64_t m, int n, int k, int num_groups, int expect
         const int64_t n_blocks = ((int64_t)n + s.block_n - 1) / s.block_n;
         const int64_t tiles = (layout == kMasked ? G : 1) * m_blocks * n_blocks;
         if (tiles > 0x7fffffff) continue;
-        const int64_t eff_m_blocks = (eff_rows + s.block_m - 1) / s.block_m;
-        const int64_t eff_tiles = (layout == kMasked ? G : 1) * eff_m_blocks * n_blocks;
-        const int64_t per_cu = (eff_tiles + num_cus - 1) / num_cus;
+        double eff_m_blocks = (double)((eff_rows + s.block_m - 1) / s.block_m);
+        if (spread > 0) {                          // mean of ceil(x / block_m), x = 1 .. spread
+            const int64_t full = spread / s.block_m, rest = spread % s.block_m;
+            double sum = (double)s.block_m * full * (full + 1) / 2.0;
+            sum += (double)rest * (full + 1);
+            eff_m_blocks = sum / spread;
+        }
+        const int64_t eff_tiles =
+            (int64_t)ceil((layout == kMasked ? G : 1) * eff_m_blocks * n_blocks - 1e-9);
+        // the schedule is static: tiles (skipped ones included) are dealt round-robin, so a
+        // CU may be handed ceil(tiles / CUs) tiles that all hold valid rows
+        const int64_t per_cu = (tiles + num_cus - 1) / num_cus;
         const double bytes = (double)G * eff_rows * k + (double)G * n * k + (double)G * eff_rows * n * 2;
-        const double t_hbm = bytes / kHbmBytesPerClk;
-        double t = per_cu * tile_cycles(s, k);
+        const double t_hbm = bytes / kHbmBytesPerNs;
+        double t = per_cu * ((k / 128) * (double)s.chunk_ns + s.tile_ns);
         if (t < t_hbm) t = t_hbm;
-        // fewer busy CUs also means fewer loads in flight: penalise under-fill
         const double fill = (double)(eff_tiles < num_cus ? eff_tiles : num_cus) / num_cus;
         t *= 1.0 + 0.1 * (1.0 - fill);
         if (best < 0 || t < best_t * (1.0 - 1e-9)) {
