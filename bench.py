@@ -67,10 +67,27 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--family", type=int, default=1, choices=sorted(FAMILY_NAMES))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=48,
+    ap.add_argument("--traffic-probe", default="",
+                    help="run only this shape (3 launches) and a 512 MiB device copy (3 launches), "
+                         "for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE passes")
+    ap.add_argument("--ingest-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn the two rocprofv3 --pmc output directories of a traffic probe into "
+                         "profiles/traffic.json")
+    ap.add_argument("--summarize-trace", default="",
+                    help="per-shape average kernel durations from a rocprofv3 --kernel-trace output "
+                         "directory of a bench.py run (dispatches attributed in launch order)")
+    ap.add_argument("--cpu-rows", type=int, default=1536,
                     help="rows of D per shape the oracle computes for the CPU baseline")
     ap.add_argument("--per-shape-out", default="", help="also write per-shape results here")
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.family)
+        return
+    if args.ingest_traffic:
+        if not args.traffic_probe:
+            raise SystemExit("--ingest-traffic needs --traffic-probe NAME (the probed shape)")
+        ingest_traffic(args.ingest_traffic[0], args.ingest_traffic[1], args.traffic_probe)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has "
               "no multi-GPU path.", file=sys.stderr)
@@ -120,6 +137,20 @@ def main():
         else:
             fp8bs.grouped_masked_nt(q["a"], q["sfa"], q["b"], q["sfb"], q["d"], q["extra"],
                                     expected_m=p.expected_m)
+
+    if args.traffic_probe:
+        sel = [q for q in problems if q["desc"]["name"] == args.traffic_probe]
+        if not sel:
+            raise SystemExit(f"no shape {args.traffic_probe} in family {args.family}")
+        src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            launch(sel[0])
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"traffic_probe": args.traffic_probe, "copy_bytes": COPY_PROBE_BYTES}))
+        return
 
     for _ in range(args.warmup):
         for q in problems:
@@ -204,6 +235,87 @@ def main():
         with open(args.per_shape_out, "w") as fh:
             json.dump(out, fh, indent=1)
     print(json.dumps(out), flush=True)
+
+
+COPY_PROBE_BYTES = 512 << 20
+
+
+def _pmc_per_dispatch(d, counter):
+    """{kernel name: [per-dispatch counter value summed over dimensions]} from a rocprofv3
+    --pmc csv output directory."""
+    import csv
+    import glob
+    import collections
+    vals = collections.defaultdict(float)
+    names = {}
+    for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            key = (r["Dispatch_Id"], r["Kernel_Name"])
+            vals[key] += float(r["Counter_Value"])
+            names[key] = r["Kernel_Name"]
+    out = collections.defaultdict(list)
+    for key in sorted(vals, key=lambda k: int(k[0])):
+        out[names[key]].append(vals[key])
+    return out
+
+
+def ingest_traffic(fetch_dir, write_dir, name):
+    """profiles/traffic.json: HBM bytes per launch of the GEMM kernel in a traffic probe,
+    FETCH_SIZE and WRITE_SIZE (KiB) scaled so that the plain copy of COPY_PROBE_BYTES
+    reads and writes exactly that many bytes."""
+    fetch = _pmc_per_dispatch(fetch_dir, "FETCH_SIZE")
+    write = _pmc_per_dispatch(write_dir, "WRITE_SIZE")
+    def pick(tab, pred):
+        ks = [k for k in tab if pred(k)]
+        if len(ks) != 1:
+            raise SystemExit(f"expected one matching kernel, found {ks}")
+        return ks[0], tab[ks[0]]
+    gk, gf = pick(fetch, lambda k: "fp8bs_gemm_kernel" in k)
+    ck, cf = pick(fetch, lambda k: "fp8bs" not in k and "copy" in k.lower())
+    _, gw = pick(write, lambda k: "fp8bs_gemm_kernel" in k)
+    _, cw = pick(write, lambda k: "fp8bs" not in k and "copy" in k.lower())
+    # the copy kernel also moved the (small) inputs to the device: keep the three largest
+    # dispatches, the COPY_PROBE_BYTES copies
+    cf, cw = sorted(cf)[-3:], sorted(cw)[-3:]
+    med = lambda v: sorted(v)[len(v) // 2]
+    fscale = COPY_PROBE_BYTES / (med(cf) * 1024.0)
+    wscale = COPY_PROBE_BYTES / (med(cw) * 1024.0)
+    fetch_b = med(gf) * 1024.0 * fscale
+    write_b = med(gw) * 1024.0 * wscale
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    data = json.load(open(path)) if os.path.exists(path) else {}
+    if data.get("source_sha256") != kernel_source_hash():
+        data = {"source_sha256": kernel_source_hash(), "shapes": {}}
+    data["shapes"][name] = {"kernel": gk, "fetch_bytes": fetch_b, "write_bytes": write_b,
+                            "bytes_per_launch": fetch_b + write_b,
+                            "copy_kernel": ck, "fetch_scale": fscale, "write_scale": wscale}
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    json.dump(data, open(path, "w"), indent=1)
+    print(json.dumps(data["shapes"][name]))
+
+
+def summarize_trace(d, family):
+    """Average duration per workload shape from a kernel trace of `bench.py --family F`:
+    the GEMM dispatches cycle through the family's shapes in order."""
+    import csv
+    import glob
+    from moe_grouped_gemm_block_amd import synth
+    names = [x["name"] for x in synth.workload_shapes(family)]
+    rows = []
+    for path in glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True):
+        rows += [r for r in csv.DictReader(open(path)) if "fp8bs_gemm_kernel" in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    per = {n: [] for n in names}
+    for i, r in enumerate(rows):
+        per[names[i % len(names)]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    out = {}
+    for n in names:
+        v = per[n]
+        out[n] = {"dispatches": len(v), "avg_us": sum(v) / max(1, len(v)),
+                  "min_us": min(v) if v else None, "max_us": max(v) if v else None}
+    print(json.dumps(out, indent=1))
 
 
 def cpu_baseline(problems, rows_per_shape: int):
