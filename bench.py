@@ -124,19 +124,26 @@ def main():
             extra = torch.from_numpy(p.layout).to(dev)
         elif p.kind == "masked":
             extra = torch.from_numpy(p.masked_m).to(dev)
-        problems.append(dict(desc=desc, p=p, a=a, sfa=sfa, b=b, sfb=sfb, d=d, extra=extra))
+        # split-K workspace, allocated once per shape outside the timed region
+        layout = {"dense": fp8bs.LAYOUT_DENSE, "contiguous": fp8bs.LAYOUT_CONTIGUOUS,
+                  "masked": fp8bs.LAYOUT_MASKED}[p.kind]
+        wsz = fp8bs.workspace_size(layout, p.max_m if p.kind == "masked" else p.M, p.N, p.K, p.G,
+                                   p.expected_m if p.kind == "masked" else 0)
+        ws = torch.empty(max(wsz, 16), dtype=torch.uint8, device=dev)
+        problems.append(dict(desc=desc, p=p, a=a, sfa=sfa, b=b, sfb=sfb, d=d, extra=extra, ws=ws))
     torch.cuda.synchronize()
     gen_s = time.time() - t0
 
     def launch(q):
         p = q["p"]
         if p.kind == "dense":
-            fp8bs.dense_nt(q["a"], q["sfa"], q["b"], q["sfb"], q["d"])
+            fp8bs.fp8bs_dense_nt_ws(q["a"], q["sfa"], q["b"], q["sfb"], q["d"], workspace=q["ws"])
         elif p.kind == "contiguous":
-            fp8bs.grouped_contiguous_nt(q["a"], q["sfa"], q["b"], q["sfb"], q["d"], q["extra"])
+            fp8bs.fp8bs_grouped_contiguous_nt_ws(q["a"], q["sfa"], q["b"], q["sfb"], q["d"],
+                                                 q["extra"], workspace=q["ws"])
         else:
-            fp8bs.grouped_masked_nt(q["a"], q["sfa"], q["b"], q["sfb"], q["d"], q["extra"],
-                                    expected_m=p.expected_m)
+            fp8bs.fp8bs_grouped_masked_nt_ws(q["a"], q["sfa"], q["b"], q["sfb"], q["d"], q["extra"],
+                                             expected_m=p.expected_m, workspace=q["ws"])
 
     if args.traffic_probe:
         sel = [q for q in problems if q["desc"]["name"] == args.traffic_probe]

@@ -36,8 +36,8 @@
  *
  * Conventions shared by every entry point:
  *   - All tensor pointers are DEVICE pointers on the current HIP device; the
- *     caller owns every buffer.  The library allocates nothing, keeps no
- *     pointer after returning and never synchronises `stream`.
+ *     caller owns every buffer (workspace included).  The library allocates
+ *     nothing, keeps no pointer after returning and never synchronises `stream`.
  *   - Calls are asynchronous on `stream` (NULL = the default stream).  Buffers
  *     must stay alive until the stream work completes.
  *   - Inputs are read-only.  D is written only at valid rows (see each call)
@@ -51,7 +51,8 @@
  *   - Errors are reported by the return value before anything is launched;
  *     nothing is printed (unless FP8BS_PRINT_CONFIGS=1) and nothing aborts.
  *     A launch failure reported by the HIP runtime maps to FP8BS_ERR_HIP.
- *   - Thread-safe.  The only global state is the CU cap (fp8bs_set_num_cus).
+ *   - Thread-safe.  The only global state is the CU cap (fp8bs_set_num_cus)
+ *     and the test pins (fp8bs_force_instance, fp8bs_force_splits).
  *   - Graph-capturable: device-side group data (grouped_layout, masked_m) is
  *     never read on the host.
  */
@@ -131,6 +132,46 @@ int fp8bs_grouped_masked_nt(const void* a, const float* sfa, const void* b, cons
                             void* d, const int32_t* masked_m, int num_groups, int max_m,
                             int expected_m, int n, int k, hipStream_t stream);
 
+/*
+ * Workspace variants.  The three calls below compute exactly what the call of
+ * the same name without "_ws" computes; they differ only in that the caller
+ * also lends `workspace` (device memory, 16-byte aligned, workspace_bytes long,
+ * contents ignored and overwritten, not needed after the stream work ends).
+ * With workspace the planner may split the K range of each output tile into S
+ * ranges of whole 128-K chunks: every (tile, range) unit writes an FP32 partial
+ * tile to the workspace, and a second kernel adds the S partials in the fixed
+ * order 0..S-1 (so results do not depend on scheduling), rounds to BF16 and
+ * stores the valid rows.  This fills the machine when M is small (decode):
+ * output tiles alone then number far fewer than compute units.  Split-K is not
+ * on the pages; it answers the under-filled-SM problem their block-size
+ * discussion raises (DeepGEMM README repost, lqnn.cn/news/60274, section
+ * "优化技术", unaligned block sizes).  Because the partial sums are added in a
+ * different association than the unsplit kernel's, results may differ from the
+ * workspace-free call in the last BF16 bit; both stay within the same bound of
+ * the exact result.  workspace may be NULL when workspace_bytes is 0 (then no
+ * split is used).  Two calls in flight at once must not share a workspace.
+ */
+int fp8bs_dense_nt_ws(const void* a, const float* sfa, const void* b, const float* sfb, void* d,
+                      int m, int n, int k, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+int fp8bs_grouped_contiguous_nt_ws(const void* a, const float* sfa, const void* b,
+                                   const float* sfb, void* d, const int32_t* grouped_layout,
+                                   int m_total, int n, int k, int num_groups, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
+int fp8bs_grouped_masked_nt_ws(const void* a, const float* sfa, const void* b, const float* sfb,
+                               void* d, const int32_t* masked_m, int num_groups, int max_m,
+                               int expected_m, int n, int k, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes the planner's preferred plan uses for a request on the current
+ * device (CU cap respected; `m` as in fp8bs_plan_query).  0 means the best plan
+ * splits nothing.  Passing at least this much to a _ws call lets it use that
+ * plan; less makes it pick the best plan that fits.  On an invalid request, a
+ * pin the request cannot use, or a HIP error it returns the negated status
+ * (-FP8BS_ERR_SHAPE, -FP8BS_ERR_UNSUPPORTED, -FP8BS_ERR_HIP). */
+int64_t fp8bs_workspace_size(int layout, int64_t m, int n, int k, int num_groups,
+                             int expected_m);
+
 /* Row alignment of expert segments in the contiguous layout (128).  Analogue
  * of get_mk_alignment_for_contiguous_layout (hada page, section "Tiện ích và
  * biến môi trường"). */
@@ -154,6 +195,14 @@ int fp8bs_get_num_cus(void);
  * setting, or -2 for an index out of range. */
 int fp8bs_force_instance(int i);
 
+/* Pins the K split count of later _ws calls to s >= 1 (1 = no split); 0
+ * restores the planner's choice.  A pinned count that the request cannot use
+ * (s > K/128, or more workspace than lent) makes the call fail with
+ * FP8BS_ERR_UNSUPPORTED.  For testing and measuring; changes speed, and
+ * results only within the bound stated for the _ws calls.  Returns the previous
+ * setting, or -1 for s < 0. */
+int fp8bs_force_splits(int s);
+
 /* Planner result for one request, as chosen by the entry points. */
 typedef struct {
     int block_m;        /* rows per output tile                               */
@@ -163,21 +212,26 @@ typedef struct {
     int threads;        /* threads per workgroup                              */
     int lds_bytes;      /* LDS per workgroup                                  */
     int wg_per_cu;      /* workgroups resident per CU the planner assumes     */
+    int stages;         /* 128-K chunks the LDS ring holds                    */
     int64_t tiles;      /* upper bound of output tiles in the schedule        */
     int64_t grid;       /* persistent workgroups launched                     */
     int raster;         /* m-blocks per raster group                          */
     int instance;       /* index of the compiled kernel instance              */
+    int splits;         /* K ranges per tile (1: no split, no workspace)      */
+    int64_t workspace_bytes; /* workspace the plan uses (0 when splits == 1)  */
 } fp8bs_plan;
 
 /*
  * Host-only planner query (no device access): the configuration the entry
  * point for `layout` would use for these sizes on a device with `num_cus`
- * compute units.  For FP8BS_LAYOUT_DENSE `m` is M; for CONTIGUOUS it is
- * m_total; for MASKED it is max_m (num_groups groups, expected_m hint).
- * Returns FP8BS_OK and fills *out, or an error status.
+ * compute units when lent `workspace_bytes` of workspace (0: the call without
+ * "_ws").  For FP8BS_LAYOUT_DENSE `m` is M; for CONTIGUOUS it is m_total; for
+ * MASKED it is max_m (num_groups groups, expected_m hint).  Returns FP8BS_OK
+ * and fills *out, or an error status.  Pins (fp8bs_force_instance,
+ * fp8bs_force_splits) are not applied here.
  */
 int fp8bs_plan_query(int layout, int64_t m, int n, int k, int num_groups, int expected_m,
-                     int num_cus, fp8bs_plan* out);
+                     int num_cus, int64_t workspace_bytes, fp8bs_plan* out);
 
 /* Output tiles a (block_m x block_n) tiling has for a request: m-blocks x
  * n-blocks (x num_groups for MASKED, where m is max_m).  Plain tile
@@ -185,14 +239,14 @@ int fp8bs_plan_query(int layout, int64_t m, int n, int k, int num_groups, int ex
 int64_t fp8bs_count_tiles(int layout, int64_t m, int n, int num_groups, int block_m, int block_n);
 
 /* Number of compiled kernel instances, and the shape of instance i (fields
- * tiles, grid and raster are 0).  fp8bs_instance_info returns FP8BS_OK or
+ * tiles, grid, raster and workspace_bytes are 0, splits is 1).  fp8bs_instance_info returns FP8BS_OK or
  * FP8BS_ERR_UNSUPPORTED for an index out of range. */
 int fp8bs_num_instances(void);
 int fp8bs_instance_info(int i, fp8bs_plan* out);
 
-/* Human-readable summary of the plan for a request on the current device's CU
- * count (respecting the cap), written to buf (NUL-terminated, truncated to
- * len).  Analogue of DG_PRINT_CONFIGS; FP8BS_PRINT_CONFIGS=1 prints the same
+/* Human-readable summary of the plan a _ws call lent fp8bs_workspace_size
+ * bytes would use for a request on the current device's CU count (respecting
+ * the cap and the pins), written to buf (NUL-terminated, truncated to len).  Analogue of DG_PRINT_CONFIGS; FP8BS_PRINT_CONFIGS=1 prints the same
  * line to stderr at every call.  Returns the status of the planner. */
 int fp8bs_describe_config(int layout, int64_t m, int n, int k, int num_groups, int expected_m,
                           char* buf, size_t len);

@@ -2,7 +2,14 @@
 
 Thin Python binding of ``libfp8bs.so`` (C ABI declared in ``include/fp8bs.h``):
 argument checks and marshalling only -- every step of the computation runs in
-the library's HIP kernels.  PyTorch supplies device memory and the stream.
+the library's HIP kernels.  PyTorch supplies device memory (the split-K
+workspace included) and the stream.
+
+``fp8bs_*_nt`` map one to one onto the C calls without workspace, and
+``fp8bs_*_nt_ws`` onto the workspace calls (a workspace tensor of
+``workspace_size(...)`` bytes is allocated on the call's stream when none is
+given).  ``dense_nt``, ``grouped_contiguous_nt`` and ``grouped_masked_nt`` are
+the workspace variants.
 
 The binding refuses to run without the compiled library; there is no fallback.
 Build it with ``python -m moe_grouped_gemm_block_amd.build``.
@@ -15,9 +22,11 @@ from typing import Optional
 
 __all__ = [
     "fp8bs_dense_nt", "fp8bs_grouped_contiguous_nt", "fp8bs_grouped_masked_nt",
+    "fp8bs_dense_nt_ws", "fp8bs_grouped_contiguous_nt_ws", "fp8bs_grouped_masked_nt_ws",
     "dense_nt", "grouped_contiguous_nt", "grouped_masked_nt",
     "get_mk_alignment", "get_sfa_ld", "set_num_cus", "get_num_cus", "plan_query",
-    "describe_config", "count_tiles", "instances", "force_instance", "status_string", "sfa_mn_major", "library_path", "FP8BSError",
+    "workspace_size", "describe_config", "count_tiles", "instances", "force_instance",
+    "force_splits", "status_string", "sfa_mn_major", "library_path", "FP8BSError",
     "LAYOUT_DENSE", "LAYOUT_CONTIGUOUS", "LAYOUT_MASKED",
 ]
 
@@ -37,8 +46,9 @@ class FP8BSError(RuntimeError):
 class _Plan(ctypes.Structure):
     _fields_ = [("block_m", ctypes.c_int), ("block_n", ctypes.c_int), ("waves_m", ctypes.c_int),
                 ("waves_n", ctypes.c_int), ("threads", ctypes.c_int), ("lds_bytes", ctypes.c_int),
-                ("wg_per_cu", ctypes.c_int), ("tiles", ctypes.c_int64), ("grid", ctypes.c_int64),
-                ("raster", ctypes.c_int), ("instance", ctypes.c_int)]
+                ("wg_per_cu", ctypes.c_int), ("stages", ctypes.c_int), ("tiles", ctypes.c_int64),
+                ("grid", ctypes.c_int64), ("raster", ctypes.c_int), ("instance", ctypes.c_int),
+                ("splits", ctypes.c_int), ("workspace_bytes", ctypes.c_int64)]
 
 
 def library_path() -> str:
@@ -57,14 +67,23 @@ def _load():
     lib.fp8bs_dense_nt.argtypes = [P, P, P, P, P, I, I, I, P]
     lib.fp8bs_grouped_contiguous_nt.argtypes = [P, P, P, P, P, P, I, I, I, I, P]
     lib.fp8bs_grouped_masked_nt.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P]
+    S = ctypes.c_size_t
+    lib.fp8bs_dense_nt_ws.argtypes = [P, P, P, P, P, I, I, I, P, S, P]
+    lib.fp8bs_grouped_contiguous_nt_ws.argtypes = [P, P, P, P, P, P, I, I, I, I, P, S, P]
+    lib.fp8bs_grouped_masked_nt_ws.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P, S, P]
     for f in ("fp8bs_dense_nt", "fp8bs_grouped_contiguous_nt", "fp8bs_grouped_masked_nt",
+              "fp8bs_dense_nt_ws", "fp8bs_grouped_contiguous_nt_ws", "fp8bs_grouped_masked_nt_ws",
               "fp8bs_get_mk_alignment", "fp8bs_set_num_cus", "fp8bs_get_num_cus",
               "fp8bs_plan_query", "fp8bs_describe_config"):
         getattr(lib, f).restype = I
     lib.fp8bs_get_sfa_ld.argtypes = [I64]
     lib.fp8bs_get_sfa_ld.restype = I64
     lib.fp8bs_set_num_cus.argtypes = [I]
-    lib.fp8bs_plan_query.argtypes = [I, I64, I, I, I, I, I, ctypes.POINTER(_Plan)]
+    lib.fp8bs_plan_query.argtypes = [I, I64, I, I, I, I, I, I64, ctypes.POINTER(_Plan)]
+    lib.fp8bs_workspace_size.argtypes = [I, I64, I, I, I, I]
+    lib.fp8bs_workspace_size.restype = I64
+    lib.fp8bs_force_splits.argtypes = [I]
+    lib.fp8bs_force_splits.restype = I
     lib.fp8bs_describe_config.argtypes = [I, I64, I, I, I, I, ctypes.c_char_p, ctypes.c_size_t]
     lib.fp8bs_count_tiles.argtypes = [I, I64, I, I, I, I]
     lib.fp8bs_count_tiles.restype = I64
@@ -100,13 +119,24 @@ def get_num_cus() -> int:
 
 
 def plan_query(layout: int, m: int, n: int, k: int, num_groups: int = 1, expected_m: int = 0,
-               num_cus: int = 256) -> dict:
+               num_cus: int = 256, workspace_bytes: int = 0) -> dict:
     plan = _Plan()
     st = _load().fp8bs_plan_query(int(layout), int(m), int(n), int(k), int(num_groups),
-                                  int(expected_m), int(num_cus), ctypes.byref(plan))
+                                  int(expected_m), int(num_cus), int(workspace_bytes),
+                                  ctypes.byref(plan))
     if st != 0:
         raise FP8BSError(st, "fp8bs_plan_query")
     return {name: getattr(plan, name) for name, _ in _Plan._fields_}
+
+
+def workspace_size(layout: int, m: int, n: int, k: int, num_groups: int = 1,
+                   expected_m: int = 0) -> int:
+    """Workspace bytes the preferred plan uses on the current device (0: no split)."""
+    v = int(_load().fp8bs_workspace_size(int(layout), int(m), int(n), int(k), int(num_groups),
+                                         int(expected_m)))
+    if v < 0:
+        raise FP8BSError(-v, "fp8bs_workspace_size")
+    return v
 
 
 def count_tiles(layout: int, m: int, n: int, num_groups: int, block_m: int, block_n: int) -> int:
@@ -129,6 +159,14 @@ def force_instance(i: int) -> int:
     prev = int(_load().fp8bs_force_instance(int(i)))
     if prev == -2:
         raise ValueError(f"no compiled instance {i}")
+    return prev
+
+
+def force_splits(s: int) -> int:
+    """Pin the K split count of later workspace calls (0 = planner's choice); returns the previous."""
+    prev = int(_load().fp8bs_force_splits(int(s)))
+    if prev == -1:
+        raise ValueError(f"invalid split count {s}")
     return prev
 
 
@@ -200,27 +238,36 @@ def _check(st: int, where: str):
         raise FP8BSError(st, where)
 
 
-def fp8bs_dense_nt(a, sfa, b, sfb, d, stream=None):
-    """D[m][n] = A[m][k] * B[n][k]^T with 1x128 A scales and 128x128 B scales.
+def _workspace(ws, layout, m, n, k, g, expected_m, stream, device):
+    """(pointer, bytes, tensor) of the workspace for a _ws call: the caller's uint8 device
+    tensor, or a fresh one of workspace_size() bytes allocated on the call's stream."""
+    torch = _torch()
+    if ws is None:
+        nbytes = workspace_size(layout, m, n, k, g, expected_m)
+        if nbytes == 0:
+            return ctypes.c_void_p(None), 0, None
+        with torch.cuda.stream(stream):
+            ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    ptr = _dev_ptr(ws, "workspace", (torch.uint8,), 1)
+    return ptr, ws.numel(), ws
 
-    a: e4m3 [m][k]; sfa: f32 MN-major [k/128][ld(m)]; b: e4m3 [n][k];
-    sfb: f32 [ceil(n/128)][k/128]; d: bf16 [m][n] (written)."""
+
+def _dense_args(a, sfa, b, sfb, d):
+    torch = _torch()
     m, k = a.shape
     n = b.shape[0]
     kb = k // 128 if k % 128 == 0 else -1
-    args = (_dev_ptr(a, "a", _fp8_dtypes(), 2), _dev_ptr(sfa, "sfa", (_torch().float32,)),
-            _dev_ptr(b, "b", _fp8_dtypes(), 2), _dev_ptr(sfb, "sfb", (_torch().float32,)),
+    args = (_dev_ptr(a, "a", _fp8_dtypes(), 2), _dev_ptr(sfa, "sfa", (torch.float32,)),
+            _dev_ptr(b, "b", _fp8_dtypes(), 2), _dev_ptr(sfb, "sfb", (torch.float32,)),
             _dev_ptr(d, "d", _bf16_dtypes(), 2))
     if b.shape[1] != k or tuple(d.shape) != (m, n):
         raise ValueError("shape mismatch between a, b and d")
     if kb > 0 and (sfa.numel() != kb * get_sfa_ld(m) or sfb.numel() != ((n + 127) // 128) * kb):
         raise ValueError("scale tensor sizes do not match the shapes")
-    _check(_load().fp8bs_dense_nt(*args, m, n, k, _stream_handle(stream, a.device)),
-           "fp8bs_dense_nt")
+    return args, m, n, k
 
 
-def fp8bs_grouped_contiguous_nt(a, sfa, b, sfb, d, grouped_layout, stream=None):
-    """Contiguous MoE layout: a [m_total][k], b [g][n][k], grouped_layout int32 [m_total]."""
+def _contiguous_args(a, sfa, b, sfb, d, grouped_layout):
     torch = _torch()
     m, k = a.shape
     g, n = b.shape[0], b.shape[1]
@@ -233,12 +280,10 @@ def fp8bs_grouped_contiguous_nt(a, sfa, b, sfb, d, grouped_layout, stream=None):
         raise ValueError("shape mismatch between a, b, d and grouped_layout")
     if kb > 0 and (sfa.numel() != kb * get_sfa_ld(m) or sfb.numel() != g * ((n + 127) // 128) * kb):
         raise ValueError("scale tensor sizes do not match the shapes")
-    _check(_load().fp8bs_grouped_contiguous_nt(*args, m, n, k, g, _stream_handle(stream, a.device)),
-           "fp8bs_grouped_contiguous_nt")
+    return args, m, n, k, g
 
 
-def fp8bs_grouped_masked_nt(a, sfa, b, sfb, d, masked_m, expected_m: int = 0, stream=None):
-    """Masked MoE layout: a [g][max_m][k], b [g][n][k], d [g][max_m][n], masked_m int32 [g]."""
+def _masked_args(a, sfa, b, sfb, d, masked_m):
     torch = _torch()
     g, max_m, k = a.shape
     n = b.shape[1]
@@ -251,11 +296,76 @@ def fp8bs_grouped_masked_nt(a, sfa, b, sfb, d, masked_m, expected_m: int = 0, st
     if kb > 0 and (sfa.numel() != g * kb * get_sfa_ld(max_m)
                    or sfb.numel() != g * ((n + 127) // 128) * kb):
         raise ValueError("scale tensor sizes do not match the shapes")
-    _check(_load().fp8bs_grouped_masked_nt(*args, g, max_m, int(expected_m), n, k,
-                                           _stream_handle(stream, a.device)),
-           "fp8bs_grouped_masked_nt")
+    return args, g, max_m, n, k
 
 
-dense_nt = fp8bs_dense_nt
-grouped_contiguous_nt = fp8bs_grouped_contiguous_nt
-grouped_masked_nt = fp8bs_grouped_masked_nt
+def _stream(stream, device):
+    torch = _torch()
+    return torch.cuda.current_stream(device) if stream is None else stream
+
+
+def fp8bs_dense_nt(a, sfa, b, sfb, d, stream=None):
+    """D[m][n] = A[m][k] * B[n][k]^T with 1x128 A scales and 128x128 B scales.
+
+    a: e4m3 [m][k]; sfa: f32 MN-major [k/128][ld(m)]; b: e4m3 [n][k];
+    sfb: f32 [ceil(n/128)][k/128]; d: bf16 [m][n] (written)."""
+    args, m, n, k = _dense_args(a, sfa, b, sfb, d)
+    with _torch().cuda.device(a.device):
+        st = _load().fp8bs_dense_nt(*args, m, n, k, _stream_handle(stream, a.device))
+    _check(st, "fp8bs_dense_nt")
+
+
+def fp8bs_dense_nt_ws(a, sfa, b, sfb, d, workspace=None, stream=None):
+    """fp8bs_dense_nt with a split-K workspace (uint8 device tensor, or None to allocate)."""
+    args, m, n, k = _dense_args(a, sfa, b, sfb, d)
+    with _torch().cuda.device(a.device):
+        s = _stream(stream, a.device)
+        wp, wb, _keep = _workspace(workspace, LAYOUT_DENSE, m, n, k, 1, 0, s, a.device)
+        st = _load().fp8bs_dense_nt_ws(*args, m, n, k, wp, wb, ctypes.c_void_p(s.cuda_stream))
+    _check(st, "fp8bs_dense_nt_ws")
+
+
+def fp8bs_grouped_contiguous_nt(a, sfa, b, sfb, d, grouped_layout, stream=None):
+    """Contiguous MoE layout: a [m_total][k], b [g][n][k], grouped_layout int32 [m_total]."""
+    args, m, n, k, g = _contiguous_args(a, sfa, b, sfb, d, grouped_layout)
+    with _torch().cuda.device(a.device):
+        st = _load().fp8bs_grouped_contiguous_nt(*args, m, n, k, g, _stream_handle(stream, a.device))
+    _check(st, "fp8bs_grouped_contiguous_nt")
+
+
+def fp8bs_grouped_contiguous_nt_ws(a, sfa, b, sfb, d, grouped_layout, workspace=None, stream=None):
+    """fp8bs_grouped_contiguous_nt with a split-K workspace."""
+    args, m, n, k, g = _contiguous_args(a, sfa, b, sfb, d, grouped_layout)
+    with _torch().cuda.device(a.device):
+        s = _stream(stream, a.device)
+        wp, wb, _keep = _workspace(workspace, LAYOUT_CONTIGUOUS, m, n, k, g, 0, s, a.device)
+        st = _load().fp8bs_grouped_contiguous_nt_ws(*args, m, n, k, g, wp, wb,
+                                                    ctypes.c_void_p(s.cuda_stream))
+    _check(st, "fp8bs_grouped_contiguous_nt_ws")
+
+
+def fp8bs_grouped_masked_nt(a, sfa, b, sfb, d, masked_m, expected_m: int = 0, stream=None):
+    """Masked MoE layout: a [g][max_m][k], b [g][n][k], d [g][max_m][n], masked_m int32 [g]."""
+    args, g, max_m, n, k = _masked_args(a, sfa, b, sfb, d, masked_m)
+    with _torch().cuda.device(a.device):
+        st = _load().fp8bs_grouped_masked_nt(*args, g, max_m, int(expected_m), n, k,
+                                             _stream_handle(stream, a.device))
+    _check(st, "fp8bs_grouped_masked_nt")
+
+
+def fp8bs_grouped_masked_nt_ws(a, sfa, b, sfb, d, masked_m, expected_m: int = 0, workspace=None,
+                               stream=None):
+    """fp8bs_grouped_masked_nt with a split-K workspace."""
+    args, g, max_m, n, k = _masked_args(a, sfa, b, sfb, d, masked_m)
+    with _torch().cuda.device(a.device):
+        s = _stream(stream, a.device)
+        wp, wb, _keep = _workspace(workspace, LAYOUT_MASKED, max_m, n, k, g, int(expected_m), s,
+                                   a.device)
+        st = _load().fp8bs_grouped_masked_nt_ws(*args, g, max_m, int(expected_m), n, k, wp, wb,
+                                                ctypes.c_void_p(s.cuda_stream))
+    _check(st, "fp8bs_grouped_masked_nt_ws")
+
+
+dense_nt = fp8bs_dense_nt_ws
+grouped_contiguous_nt = fp8bs_grouped_contiguous_nt_ws
+grouped_masked_nt = fp8bs_grouped_masked_nt_ws

@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <cstdint>
 
 #include "fp8bs_internal.h"
 
@@ -14,6 +15,7 @@ namespace {
 
 std::atomic<int> g_cu_cap{0};
 std::atomic<int> g_forced_instance{-1};
+std::atomic<int> g_forced_splits{0};
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_dev_cus[kMaxDevices];   // 0 = not queried yet
 
@@ -47,32 +49,46 @@ void format_plan(const fp8bs::Plan& pl, int layout, int64_t m, int n, int k, int
     static const char* names[3] = {"dense", "contiguous", "masked"};
     snprintf(buf, len,
              "fp8bs %s m=%lld n=%d k=%d groups=%d expected_m=%d cus=%d -> block %dx%d "
-             "waves %dx%d threads %d lds %dB wg/cu %d tiles %lld grid %lld raster %d instance %d",
+             "waves %dx%d threads %d stages %d lds %dB wg/cu %d tiles %lld splits %d "
+             "workspace %lldB grid %lld raster %d instance %d",
              names[layout], (long long)m, n, k, g, expected_m, cus, pl.shape.block_m,
              pl.shape.block_n, pl.shape.waves_m, pl.shape.waves_n,
-             64 * pl.shape.waves_m * pl.shape.waves_n, pl.shape.lds_bytes, pl.shape.wg_per_cu,
-             (long long)pl.tiles, (long long)pl.grid, pl.raster, pl.instance);
+             64 * pl.shape.waves_m * pl.shape.waves_n, pl.shape.stages, pl.shape.lds_bytes,
+             pl.shape.wg_per_cu, (long long)pl.tiles, pl.splits, (long long)pl.workspace_bytes,
+             (long long)pl.grid, pl.raster, pl.instance);
+}
+
+// Plan for a request on the current device, honouring the test pins.
+int make_plan(int layout, int64_t m, int n, int k, int num_groups, int expected_m,
+              int64_t ws_bytes, int* cus_out, fp8bs::Plan* pl) {
+    const int cus = current_num_cus();
+    if (cus <= 0) return FP8BS_ERR_HIP;
+    *cus_out = cus;
+    int st = fp8bs::plan_request(layout, m, n, k, num_groups, expected_m, cus, ws_bytes, pl);
+    if (st != FP8BS_OK) return st;
+    const int forced = g_forced_instance.load(std::memory_order_relaxed);
+    const int splits = ws_bytes > 0 ? g_forced_splits.load(std::memory_order_relaxed) : 1;
+    if (forced >= 0 || splits > 0)
+        st = fp8bs::plan_instance(forced >= 0 ? forced : pl->instance, splits, layout, m, n, k,
+                                  num_groups, expected_m, cus, ws_bytes, pl);
+    return st;
 }
 
 int run(int layout, const void* a, const float* sfa, const void* b, const float* sfb, void* d,
         const int32_t* group_data, int64_t m, int n, int k, int num_groups, int expected_m,
-        hipStream_t stream) {
+        void* ws, size_t ws_bytes, hipStream_t stream) {
     int st = fp8bs::validate_sizes(layout, m, n, k, num_groups);
     if (st != FP8BS_OK) return st;
     if (!aligned16(a) || !aligned16(sfa) || !aligned16(b) || !aligned16(sfb) || !aligned16(d))
         return FP8BS_ERR_POINTER;
     if (layout != fp8bs::kDense && !aligned4(group_data)) return FP8BS_ERR_POINTER;
+    if (ws_bytes > 0 && !aligned16(ws)) return FP8BS_ERR_POINTER;
     if (m == 0) return FP8BS_OK;
-    const int cus = current_num_cus();
-    if (cus <= 0) return FP8BS_ERR_HIP;
+    const int64_t ws_cap = ws_bytes > (size_t)INT64_MAX ? INT64_MAX : (int64_t)ws_bytes;
+    int cus = 0;
     fp8bs::Plan pl;
-    st = fp8bs::plan_request(layout, m, n, k, num_groups, expected_m, cus, &pl);
+    st = make_plan(layout, m, n, k, num_groups, expected_m, ws_cap, &cus, &pl);
     if (st != FP8BS_OK) return st;
-    const int forced = g_forced_instance.load(std::memory_order_relaxed);
-    if (forced >= 0) {
-        st = fp8bs::plan_instance(forced, layout, m, n, num_groups, cus, &pl);
-        if (st != FP8BS_OK) return st;
-    }
     if (print_configs()) {
         char line[512];
         format_plan(pl, layout, m, n, k, num_groups, expected_m, cus, line, sizeof line);
@@ -95,6 +111,9 @@ int run(int layout, const void* a, const float* sfa, const void* b, const float*
     p.n_blocks = (n + pl.shape.block_n - 1) / pl.shape.block_n;
     p.tiles = (int)pl.tiles;
     p.raster = pl.raster;
+    p.splits = pl.splits;
+    p.units = (int)(pl.tiles * pl.splits);
+    p.ws = pl.splits > 1 ? (float*)ws : nullptr;
     const int err = fp8bs::launch_instance(pl, layout, p, stream);
     return err == (int)hipSuccess ? FP8BS_OK : FP8BS_ERR_HIP;
 }
@@ -105,14 +124,14 @@ extern "C" {
 
 int fp8bs_dense_nt(const void* a, const float* sfa, const void* b, const float* sfb, void* d,
                    int m, int n, int k, hipStream_t stream) {
-    return run(fp8bs::kDense, a, sfa, b, sfb, d, nullptr, m, n, k, 1, 0, stream);
+    return run(fp8bs::kDense, a, sfa, b, sfb, d, nullptr, m, n, k, 1, 0, nullptr, 0, stream);
 }
 
 int fp8bs_grouped_contiguous_nt(const void* a, const float* sfa, const void* b, const float* sfb,
                                 void* d, const int32_t* grouped_layout, int m_total, int n, int k,
                                 int num_groups, hipStream_t stream) {
     return run(fp8bs::kContiguous, a, sfa, b, sfb, d, grouped_layout, m_total, n, k, num_groups,
-               0, stream);
+               0, nullptr, 0, stream);
 }
 
 int fp8bs_grouped_masked_nt(const void* a, const float* sfa, const void* b, const float* sfb,
@@ -120,7 +139,46 @@ int fp8bs_grouped_masked_nt(const void* a, const float* sfa, const void* b, cons
                             int expected_m, int n, int k, hipStream_t stream) {
     if (num_groups < 1) return FP8BS_ERR_SHAPE;
     return run(fp8bs::kMasked, a, sfa, b, sfb, d, masked_m, max_m, n, k, num_groups, expected_m,
-               stream);
+               nullptr, 0, stream);
+}
+
+int fp8bs_dense_nt_ws(const void* a, const float* sfa, const void* b, const float* sfb, void* d,
+                      int m, int n, int k, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+    return run(fp8bs::kDense, a, sfa, b, sfb, d, nullptr, m, n, k, 1, 0, workspace,
+               workspace_bytes, stream);
+}
+
+int fp8bs_grouped_contiguous_nt_ws(const void* a, const float* sfa, const void* b,
+                                   const float* sfb, void* d, const int32_t* grouped_layout,
+                                   int m_total, int n, int k, int num_groups, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
+    return run(fp8bs::kContiguous, a, sfa, b, sfb, d, grouped_layout, m_total, n, k, num_groups,
+               0, workspace, workspace_bytes, stream);
+}
+
+int fp8bs_grouped_masked_nt_ws(const void* a, const float* sfa, const void* b, const float* sfb,
+                               void* d, const int32_t* masked_m, int num_groups, int max_m,
+                               int expected_m, int n, int k, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+    if (num_groups < 1) return FP8BS_ERR_SHAPE;
+    return run(fp8bs::kMasked, a, sfa, b, sfb, d, masked_m, max_m, n, k, num_groups, expected_m,
+               workspace, workspace_bytes, stream);
+}
+
+int64_t fp8bs_workspace_size(int layout, int64_t m, int n, int k, int num_groups,
+                             int expected_m) {
+    if (layout < 0 || layout > 2) return -FP8BS_ERR_UNSUPPORTED;
+    const int g = layout == fp8bs::kDense ? 1 : num_groups;
+    int st = fp8bs::validate_sizes(layout, m, n, k, g);
+    if (st != FP8BS_OK) return -st;
+    if (m == 0) return 0;
+    int cus = 0;
+    fp8bs::Plan pl;
+    // the planner's choice with unlimited workspace, then any pins
+    st = make_plan(layout, m, n, k, g, expected_m, INT64_MAX, &cus, &pl);
+    if (st != FP8BS_OK) return -st;
+    return pl.workspace_bytes;
 }
 
 int fp8bs_set_num_cus(int n) {
@@ -135,15 +193,19 @@ int fp8bs_force_instance(int i) {
     return g_forced_instance.exchange(i);
 }
 
+int fp8bs_force_splits(int s) {
+    if (s < 0) return -1;
+    return g_forced_splits.exchange(s);
+}
+
 int fp8bs_describe_config(int layout, int64_t m, int n, int k, int num_groups, int expected_m,
                           char* buf, size_t len) {
     if (!buf || len == 0) return FP8BS_ERR_POINTER;
     if (layout < 0 || layout > 2) return FP8BS_ERR_UNSUPPORTED;
     const int g = layout == fp8bs::kDense ? 1 : num_groups;
-    const int cus = current_num_cus();
-    if (cus <= 0) return FP8BS_ERR_HIP;
+    int cus = 0;
     fp8bs::Plan pl;
-    const int st = fp8bs::plan_request(layout, m, n, k, g, expected_m, cus, &pl);
+    const int st = make_plan(layout, m, n, k, g, expected_m, INT64_MAX, &cus, &pl);
     if (st != FP8BS_OK) {
         snprintf(buf, len, "%s", fp8bs_status_string(st));
         return st;

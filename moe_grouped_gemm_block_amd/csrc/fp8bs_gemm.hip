@@ -1,23 +1,25 @@
-// fp8bs_gemm.hip -- the block-scaled FP8 GEMM kernel for gfx950 (CDNA4).
+// fp8bs_gemm.hip -- the block-scaled FP8 GEMM kernels for gfx950 (CDNA4).
 //
 // One kernel template serves the dense, contiguous-grouped and masked-grouped
 // layouts (the DeepGEMM README repost, lqnn.cn/news/60274, sections
 // "DeepGEMM" and "优化技术": one core kernel and one block scheduler for the
 // grouped and non-grouped GEMMs).  Per output tile and per 128-wide K chunk:
 //
-//   1. The A tile (block_m x 128 e4m3), the B tile (block_n x 128 e4m3) and the
-//      block_m A scales of the chunk are copied global -> LDS by direct-to-LDS
-//      loads (global_load_lds_dwordx4), two stages deep: while the chunk in one
-//      stage is multiplied, the next chunk -- of this tile or of the next tile
-//      the workgroup owns -- streams into the other.
+//   1. The A tile (block_m x 128 e4m3), the B tile (block_n x 128 e4m3), the
+//      tile's block_m A scales and its B-scale values are copied global -> LDS
+//      by direct-to-LDS loads (global_load_lds_dwordx4 / _dword) into a ring of
+//      NS stages: while one chunk is multiplied, the next NS-1 chunks -- of
+//      this work unit or of the next ones the workgroup owns -- stream in.
 //   2. Each wavefront multiplies its sub-tile with v_mfma_f32_16x16x128_f8f6f4
 //      (OCP e4m3 x e4m3, FP32 result), one instruction per 16x16 output block
 //      per chunk, into a partial that starts from zero every chunk.
 //   3. The partial is promoted into the FP32 accumulator on the vector ALU:
 //      acc += partial * (sfa[row] * sfb[column block]) -- the two-level
 //      accumulation of the same page's "DeepGEMM" section.
-//   4. After the last chunk the accumulator is rounded to BF16 (nearest even)
-//      and stored, only at valid rows and columns.
+//   4. After the unit's last chunk the accumulator is rounded to BF16 (nearest
+//      even) and stored at valid rows and columns, or -- when the planner splits
+//      K -- stored as an FP32 partial that fp8bs_splitk_reduce adds up in a
+//      fixed order.
 //
 // MFMA operand roles are transposed: B rows feed the instruction's first
 // operand and A rows its second, so each lane's four results share one A row
@@ -26,11 +28,12 @@
 // TM consecutive A rows across its TM row blocks, so its row scales are one
 // contiguous LDS read.
 //
-// The schedule is persistent: workgroup w processes tiles w, w + grid, ... in
-// a rasterised order (groups of `raster` m-blocks sweep the n-blocks so that
-// concurrent tiles share A and B stripes in L2), with workgroup ids remapped so
-// that each XCD (workgroups are dealt to the 8 XCDs round-robin) runs a
-// contiguous range of that order.
+// The schedule is persistent: workgroup w processes work units w, w + grid, ...
+// A unit is (K split s, tile t), split-major so that concurrent units share the
+// K range; tiles are rasterised (groups of `raster` m-blocks sweep the n-blocks
+// so that concurrent tiles share A and B stripes in L2), and workgroup ids are
+// remapped so that each XCD (workgroups are dealt to the 8 XCDs round-robin)
+// runs a contiguous range of that order.
 #include <hip/hip_runtime.h>
 
 #include "fp8bs_internal.h"
@@ -59,11 +62,13 @@ __device__ __forceinline__ f32x4 mfma_e4m3(const i32x8& first, const i32x8& seco
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(first, second, zero, 0, 0, 0, 0, 0, 0);
 }
 
-// Wait until this wavefront has no vector-memory operation (direct-to-LDS copies
-// included) and no LDS / scalar-memory operation outstanding.
-__device__ __forceinline__ void wait_loads_all() {
+// Wait until this wavefront has at most N vector-memory operations (direct-to-LDS
+// copies included) and no LDS / scalar-memory operation outstanding.
+template <int N>
+__device__ __forceinline__ void wait_loads() {
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
     // gfx9 s_waitcnt layout: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[15:14]
-    __builtin_amdgcn_s_waitcnt(0x0070);
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
 }
 
 // Workgroup barrier without a memory fence: the explicit waits before it make this
@@ -137,14 +142,69 @@ __device__ __forceinline__ bool tile_at(const GemmParams& p, int t, Tile& tl) {
     return true;
 }
 
+// A work unit: K split s of tile t, chunks [c0, c1).
+struct Unit {
+    int u, t, s, c0, c1;
+    Tile tl;
+};
+
 template <int BM, int BN, int LAYOUT>
-__device__ __forceinline__ int next_valid_tile(const GemmParams& p, int t, Tile& tl) {
-    for (; t < p.tiles; t += gridDim.x)
-        if (tile_at<BM, BN, LAYOUT>(p, t, tl)) return t;
-    return -1;
+__device__ __forceinline__ bool next_unit(const GemmParams& p, int u, Unit& w) {
+    const int kchunks = p.k / 128;
+    for (; u < p.units; u += gridDim.x) {
+        const int s = u / p.tiles, t = u - s * p.tiles;
+        if (!tile_at<BM, BN, LAYOUT>(p, t, w.tl)) continue;
+        w.u = u;
+        w.t = t;
+        w.s = s;
+        w.c0 = (int)((int64_t)s * kchunks / p.splits);
+        w.c1 = (int)((int64_t)(s + 1) * kchunks / p.splits);
+        return true;
+    }
+    return false;
 }
 
-template <int BM, int BN, int WM, int WN, int LAYOUT>
+// Rows / columns this lane holds in a tile and the BF16 store of an accumulator set:
+// lane (j = l%16, quarter kq = l/16) of wavefront (wm, wn) owns rows
+// m0 + wm*WTM + TM*j + (i ^ flip) and columns n0 + wn*WTN + 16*jn + 4*kq .. +3.
+template <int TM, int TN, int WTM, int WTN, int LAYOUT>
+__device__ __forceinline__ void store_tile(const GemmParams& p, const Tile& tl, const f32x4 (&acc)[TM][TN],
+                                           int wm, int wn, int lj, int kq, int flip) {
+    uint16_t* d_g = p.d + (LAYOUT == kMasked ? (int64_t)tl.g * p.m * p.n : (int64_t)0);
+    const bool vec_ok = (p.n & 3) == 0;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int row = tl.m0 + wm * WTM + TM * lj + (i ^ flip);
+        bool ok = row < tl.row_limit;
+        if (LAYOUT == kContiguous && ok) ok = p.grouped_layout[row] == tl.g;
+        if (!ok) continue;
+        uint16_t* drow = d_g + (int64_t)row * p.n;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int col = tl.n0 + wn * WTN + 16 * j + 4 * kq;
+            const f32x4 v = acc[i][j];
+            if (vec_ok && col + 3 < p.n) {
+                uint2 w;
+                w.x = pack_bf16x2(v[0], v[1]);
+                w.y = pack_bf16x2(v[2], v[3]);
+                *(uint2*)(drow + col) = w;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (col + e < p.n) drow[col + e] = to_bf16(v[e]);
+            }
+        }
+    }
+}
+
+// Offset (in f32x4) of accumulator (i, j) of this thread inside one unit's FP32 partial
+// tile in the workspace: [wavefront][i][j][lane], so a wavefront's store is contiguous.
+template <int TM, int TN>
+__device__ __forceinline__ int partial_index(int wave, int i, int j, int lane) {
+    return ((wave * TM + i) * TN + j) * 64 + lane;
+}
+
+template <int BM, int BN, int WM, int WN, int NS, int LAYOUT>
 __global__ void __launch_bounds__(64 * WM * WN) fp8bs_gemm_kernel(GemmParams p) {
     constexpr int NW = WM * WN;                      // wavefronts per workgroup
     constexpr int WTM = BM / WM, WTN = BN / WN;      // wavefront sub-tile
@@ -152,15 +212,23 @@ __global__ void __launch_bounds__(64 * WM * WN) fp8bs_gemm_kernel(GemmParams p) 
     static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wavefront tile must be a multiple of 16");
     static_assert(BM % 8 == 0 && BN % 8 == 0 && BM <= 256, "tile shape");
     static_assert(TM == 1 || TM == 2 || TM == 4 || TM == 8, "row blocks per wavefront");
+    static_assert(NS >= 2, "at least two stages");
     constexpr int A_OFF = 0, B_OFF = BM * 128, SA_OFF = (BM + BN) * 128, SB_OFF = SA_OFF + BM * 4;
     constexpr int STAGE = stage_bytes(BM, BN);
     constexpr int A_INS = BM / 8, B_INS = BN / 8;    // 1 KB (8 rows) per wavefront copy
     constexpr int A_PER = (A_INS + NW - 1) / NW, B_PER = (B_INS + NW - 1) / NW;
+    static_assert(A_INS >= NW && B_INS >= NW, "every wavefront must own at least one A and one B copy");
+    static_assert(NS * STAGE <= kLdsBytesPerCu, "LDS ring too large");
     constexpr int SB_SPAN = BN / 128 + 2;            // B-scale blocks a tile can touch
+    // Every wavefront issues the same number of copies per chunk (A_PER + B_PER + one
+    // scale copy; a wavefront with no copy left repeats one, writing identical bytes),
+    // so "chunk q+1 has landed" is a constant vmcnt after the copies of NS-2 later chunks.
+    constexpr int OPC = A_PER + B_PER + 1;
+    static_assert((NS - 2) * OPC <= 63, "vmcnt range");
     // the wave's columns lie in one 128-column scale block for every tile
     constexpr bool UNIFORM_SB = (BN % 128 == 0) && (128 % WTN == 0);
 
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -202,19 +270,15 @@ __global__ void __launch_bounds__(64 * WM * WN) fp8bs_gemm_kernel(GemmParams p) 
 
     // ---- copies: wavefront copy `ins` moves tile rows 8*ins .. 8*ins+7; lane L fills LDS
     // slot L%8 of row 8*ins + L/8 with the global 16-byte unit (slot ^ key(row)) ----
-    const int cp_row = lane >> 3, cp_slot = lane & 7;
-    int sb_blk0 = 0;                                  // first B-scale block of the issue tile
-    auto prepare = [&](const Tile& tl) { sb_blk0 = tl.n0 / 128; };
-
-    // copy chunk c of tile `tl` into stage s (per-lane offsets recomputed: registers are
-    // scarcer than the few address instructions)
     // The swizzle key of a copied row is the same for rows r and r + 8*NW, so the lane
     // offset of every copy of a tile is one value plus a uniform multiple of 8*NW rows.
     static_assert((TM == 1 || NW % TM == 0) && NW % 2 == 0, "copy offsets must repeat");
+    const int cp_row = lane >> 3, cp_slot = lane & 7;
     const uint32_t a_lane = (uint32_t)(8 * wave + cp_row) * (uint32_t)K +
                             (uint32_t)((cp_slot ^ a_key<TM>(8 * wave + cp_row)) << 4);
     const uint32_t b_lane = (uint32_t)(8 * wave + cp_row) * (uint32_t)K +
                             (uint32_t)((cp_slot ^ b_key(8 * wave + cp_row)) << 4);
+    // copy chunk c of tile `tl` into stage s
     auto issue = [&](const Tile& tl, int c, int s) {
         uint8_t* st = smem + s * STAGE;
         const uint8_t* a_base = p.a + (LAYOUT == kMasked ? (int64_t)tl.g * p.m * K : (int64_t)0) +
@@ -224,51 +288,49 @@ __global__ void __launch_bounds__(64 * WM * WN) fp8bs_gemm_kernel(GemmParams p) 
             const uint8_t* a_t = a_base + (int64_t)tl.m0 * K;
 #pragma unroll
             for (int k = 0; k < A_PER; ++k) {
-                const int ins = wave + k * NW;
-                if (A_INS % NW == 0 || ins < A_INS)
-                    dma16(a_t + (int64_t)k * 8 * NW * K + a_lane, (LDS_AS void*)(st + A_OFF + ins * 1024));
+                const int kk = (A_INS % NW == 0 || wave + k * NW < A_INS) ? k : k - 1;
+                dma16(a_t + (int64_t)kk * 8 * NW * K + a_lane,
+                      (LDS_AS void*)(st + A_OFF + (wave + kk * NW) * 1024));
             }
         } else {
 #pragma unroll
             for (int k = 0; k < A_PER; ++k) {
-                const int ins = wave + k * NW;
-                if (A_INS % NW == 0 || ins < A_INS) {
-                    const int row = 8 * ins + cp_row;
-                    const int grow = min(tl.m0 + row, tl.row_limit - 1);
-                    const uint32_t off = (uint32_t)grow * (uint32_t)K + (uint32_t)((cp_slot ^ a_key<TM>(row)) << 4);
-                    dma16(a_base + off, (LDS_AS void*)(st + A_OFF + ins * 1024));
-                }
+                const int ins = (A_INS % NW == 0 || wave + k * NW < A_INS) ? wave + k * NW : A_INS - 1;
+                const int row = 8 * ins + cp_row;
+                const int grow = min(tl.m0 + row, tl.row_limit - 1);
+                const uint32_t off = (uint32_t)grow * (uint32_t)K + (uint32_t)((cp_slot ^ a_key<TM>(row)) << 4);
+                dma16(a_base + off, (LDS_AS void*)(st + A_OFF + ins * 1024));
             }
         }
         if (tl.n0 + BN <= p.n) {
             const uint8_t* b_t = b_base + (int64_t)tl.n0 * K;
 #pragma unroll
             for (int k = 0; k < B_PER; ++k) {
-                const int ins = wave + k * NW;
-                if (B_INS % NW == 0 || ins < B_INS)
-                    dma16(b_t + (int64_t)k * 8 * NW * K + b_lane, (LDS_AS void*)(st + B_OFF + ins * 1024));
+                const int kk = (B_INS % NW == 0 || wave + k * NW < B_INS) ? k : k - 1;
+                dma16(b_t + (int64_t)kk * 8 * NW * K + b_lane,
+                      (LDS_AS void*)(st + B_OFF + (wave + kk * NW) * 1024));
             }
         } else {
 #pragma unroll
             for (int k = 0; k < B_PER; ++k) {
-                const int ins = wave + k * NW;
-                if (B_INS % NW == 0 || ins < B_INS) {
-                    const int row = 8 * ins + cp_row;
-                    const int grow = min(tl.n0 + row, p.n - 1);
-                    const uint32_t off = (uint32_t)grow * (uint32_t)K + (uint32_t)((cp_slot ^ b_key(row)) << 4);
-                    dma16(b_base + off, (LDS_AS void*)(st + B_OFF + ins * 1024));
-                }
+                const int ins = (B_INS % NW == 0 || wave + k * NW < B_INS) ? wave + k * NW : B_INS - 1;
+                const int row = 8 * ins + cp_row;
+                const int grow = min(tl.n0 + row, p.n - 1);
+                const uint32_t off = (uint32_t)grow * (uint32_t)K + (uint32_t)((cp_slot ^ b_key(row)) << 4);
+                dma16(b_base + off, (LDS_AS void*)(st + B_OFF + ins * 1024));
             }
         }
         if (wave == NW - 1) {
-            // the chunk's block_m A scales (MN-major: contiguous) and the B-scale values of
-            // the column blocks the tile touches
+            // the chunk's block_m A scales (MN-major: contiguous)
             const uint8_t* sa_base = (const uint8_t*)(p.sfa +
                 (LAYOUT == kMasked ? (int64_t)tl.g * kchunks * p.sfa_ld : (int64_t)0) +
                 (int64_t)c * p.sfa_ld);
             int r4 = tl.m0 + 4 * lane;                // rows past the scale array are unused
             if (r4 >= p.sfa_ld) r4 = 0;
             if (4 * lane < BM) dma16(sa_base + (uint32_t)r4 * 4u, (LDS_AS void*)(st + SA_OFF));
+        } else {
+            // the B-scale values of the column blocks the tile touches (every other
+            // wavefront writes the same bytes)
             const uint8_t* sb_base = (const uint8_t*)(p.sfb + (int64_t)tl.g * nsb * kchunks + c);
             const uint32_t sb_off = (uint32_t)min(tl.n0 / 128 + lane, nsb - 1) * (uint32_t)kchunks * 4u;
             if (lane < SB_SPAN)
@@ -294,9 +356,6 @@ __global__ void __launch_bounds__(64 * WM * WN) fp8bs_gemm_kernel(GemmParams p) 
     constexpr bool STREAM_A = TM >= TN;
     constexpr int NO = STREAM_A ? TM : TN;             // streamed blocks
     constexpr int NI = STREAM_A ? TN : TM;             // resident blocks
-
-    // registers holding one chunk's operands: resident fragments, the first streamed
-    // fragment, and the promotion scales sc[i][j] = sfa(row block i) * sfb(column block j)
     struct ChunkRegs {
         i32x8 res[NI];
         i32x8 first;
@@ -305,7 +364,7 @@ __global__ void __launch_bounds__(64 * WM * WN) fp8bs_gemm_kernel(GemmParams p) 
         float sa[TM];
         float sb[UNIFORM_SB ? 1 : TN];
     };
-    auto load_scales = [&](const uint8_t* st, const Tile& tl, int blk0, ScaleRegs& r) {
+    auto load_scales = [&](const uint8_t* st, const Tile& tl, ScaleRegs& r) {
         const float* sap = (const float*)(st + sa_rd);
 #pragma unroll
         for (int i = 0; i < TM; ++i) r.sa[i] = sap[i];
@@ -318,6 +377,7 @@ __global__ void __launch_bounds__(64 * WM * WN) fp8bs_gemm_kernel(GemmParams p) 
             }
         }
         const float* sbl = (const float*)(st + SB_OFF);
+        const int blk0 = tl.n0 / 128;
         if (UNIFORM_SB) {
             r.sb[0] = sbl[min(tl.n0 + wn * WTN, p.n - 1) / 128 - blk0];
         } else {
@@ -327,9 +387,24 @@ __global__ void __launch_bounds__(64 * WM * WN) fp8bs_gemm_kernel(GemmParams p) 
         }
     };
 
-    Tile cur;
-    int t = next_valid_tile<BM, BN, LAYOUT>(p, logical_block_id(), cur);
-    if (t < 0) return;
+    // ---- the two cursors over this workgroup's (unit, chunk) stream ----
+    Unit cur;                                          // the chunk being multiplied
+    if (!next_unit<BM, BN, LAYOUT>(p, logical_block_id(), cur)) return;
+    Unit isu = cur;                                    // the next chunk to copy
+    int ic = cur.c0;
+    bool live = true;                                  // false: stream exhausted, repeat last
+    auto advance_issue = [&]() {
+        if (!live) return;
+        if (++ic < isu.c1) return;
+        Unit nx;
+        if (next_unit<BM, BN, LAYOUT>(p, isu.u + gridDim.x, nx)) {
+            isu = nx;
+            ic = nx.c0;
+        } else {
+            live = false;                              // keep copying the last chunk (harmless)
+            ic = isu.c1 - 1;
+        }
+    };
 
     f32x4 acc[TM][TN];
 #pragma unroll
@@ -337,49 +412,34 @@ __global__ void __launch_bounds__(64 * WM * WN) fp8bs_gemm_kernel(GemmParams p) 
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    prepare(cur);
-    issue(cur, 0, 0);
-    int cur_sb_blk0 = sb_blk0;
-    wait_loads_all();
-    block_barrier();                                   // chunk 0 of the first tile is in stage 0
+    // prologue: chunks 0 .. NS-2 of the stream into stages 0 .. NS-2
+#pragma unroll
+    for (int q = 0; q < NS - 1; ++q) {
+        issue(isu.tl, ic, q);
+        advance_issue();
+    }
+    wait_loads<(NS - 2) * OPC>();
+    block_barrier();                                   // chunk 0 is in stage 0
     ChunkRegs cr;
 #pragma unroll
     for (int q = 0; q < NI; ++q) cr.res[q] = STREAM_A ? load_b(smem, q) : load_a(smem, q);
     cr.first = STREAM_A ? load_a(smem, 0) : load_b(smem, 0);
 
-    int c = 0, s = 0;
+    int c = cur.c0;
+    int sq = 0;                                        // stage of the chunk being multiplied
+    int si = NS - 1;                                   // stage the next copy goes to
     for (;;) {
-        // Invariant: chunk c of tile `cur` is in stage s and its resident fragments, first
-        // streamed fragment and scales are loaded (or in flight) in `cr`; every wavefront
-        // has finished reading stage s^1.
-        const bool last = c + 1 == kchunks;
-        // contiguous layout: which of this lane's rows belong to the tile's expert
-        uint32_t row_ok_bits = 0;
-        if (last) {
-#pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                const int row = cur.m0 + wm * WTM + TM * lj + (i ^ flip);
-                bool ok = row < cur.row_limit;
-                if (LAYOUT == kContiguous && ok) ok = p.grouped_layout[row] == cur.g;
-                row_ok_bits |= (ok ? 1u : 0u) << i;
-            }
-        }
-        Tile nxt = cur;
-        int nt = t, nc = c + 1;
-        bool have_next = true;
-        if (last) {
-            nc = 0;
-            nt = next_valid_tile<BM, BN, LAYOUT>(p, t + gridDim.x, nxt);
-            have_next = nt >= 0;
-            if (have_next) prepare(nxt);
-        }
-        if (have_next) issue(nxt, nc, s ^ 1);
+        // Invariant: chunk c of unit `cur` is in stage sq with its resident fragments and
+        // first streamed fragment loaded (or in flight) in `cr`; every wavefront has
+        // finished reading stage si, the one chunk c+NS-1 of the stream goes to.
+        issue(isu.tl, ic, si);
+        advance_issue();
 
-        const uint8_t* st = smem + s * STAGE;
+        const uint8_t* st = smem + sq * STAGE;
         float sc[TM][UNIFORM_SB ? 1 : TN];
         {
             ScaleRegs sr;
-            load_scales(st, cur, cur_sb_blk0, sr);
+            load_scales(st, cur.tl, sr);
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -415,16 +475,17 @@ __global__ void __launch_bounds__(64 * WM * WN) fp8bs_gemm_kernel(GemmParams p) 
             fr = next_fr;
         }
 
-        // ---- last block: every read of stage s has been issued.  Wait for them and for
+        // ---- last block: every read of stage sq has been issued.  Wait for them and for
         // this wavefront's copies of the next chunk, meet the other wavefronts, then start
-        // reading the next chunk while the last products of this chunk issue ----
-        // (Branch free: after the last chunk the barrier and the reads are harmless, and one
-        // basic block lets the scheduler interleave the whole chunk.)
-        wait_loads_all();
+        // reading the next chunk while the last products of this chunk issue.  (Branch
+        // free: after the last chunk the barrier and the reads are harmless, and one basic
+        // block lets the scheduler interleave the whole chunk.) ----
+        wait_loads<(NS - 2) * OPC>();
         block_barrier();
+        const int sn = sq + 1 == NS ? 0 : sq + 1;
         ChunkRegs nr;
         {
-            const uint8_t* nst = smem + (s ^ 1) * STAGE;
+            const uint8_t* nst = smem + sn * STAGE;
 #pragma unroll
             for (int q = 0; q < NI; ++q) {
                 step(NO - 1, q, fr, cr.res);   // frees resident fragment q ...
@@ -437,42 +498,71 @@ __global__ void __launch_bounds__(64 * WM * WN) fp8bs_gemm_kernel(GemmParams p) 
                 if (k >= 0) promote(k / NI, k % NI, ring[k % (LAG + 1)]);
         }
 
-        if (last) {
-            // ---- epilogue: BF16 at valid rows / columns only ----
-            uint16_t* d_g = p.d + (LAYOUT == kMasked ? (int64_t)cur.g * p.m * p.n : (int64_t)0);
-            const bool vec_ok = (p.n & 3) == 0;
+        if (c + 1 == cur.c1) {
+            // ---- end of the unit: BF16 to D, or the FP32 partial to the workspace ----
+            // lane-derived offsets are recomputed here from an opaque copy of the lane id, so
+            // that the compiler cannot hoist one register per store out of the main loop
+            int el = lane;
+            asm volatile("" : "+v"(el));
+            if (p.splits == 1) {
+                const int elj = el & 15;
+                store_tile<TM, TN, WTM, WTN, LAYOUT>(p, cur.tl, acc, wm, wn, elj, el >> 4,
+                                                     (TM > 1) ? (elj >> 3) : 0);
+            } else {
+                f32x4* ws = (f32x4*)(p.ws + ((int64_t)cur.t * p.splits + cur.s) * (BM * BN));
 #pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                if (row_ok_bits & (1u << i)) {
-                    const int row = cur.m0 + wm * WTM + TM * lj + (i ^ flip);
-                    uint16_t* drow = d_g + (int64_t)row * p.n;
+                for (int i = 0; i < TM; ++i)
 #pragma unroll
-                    for (int j = 0; j < TN; ++j) {
-                        const int col = cur.n0 + wn * WTN + 16 * j + 4 * kq;
-                        const f32x4 v = acc[i][j];
-                        if (vec_ok && col + 3 < p.n) {
-                            uint2 w;
-                            w.x = pack_bf16x2(v[0], v[1]);
-                            w.y = pack_bf16x2(v[2], v[3]);
-                            *(uint2*)(drow + col) = w;
-                        } else {
+                    for (int j = 0; j < TN; ++j) ws[partial_index<TM, TN>(wave, i, j, el)] = acc[i][j];
+            }
 #pragma unroll
-                            for (int e = 0; e < 4; ++e)
-                                if (col + e < p.n) drow[col + e] = to_bf16(v[e]);
-                        }
-                    }
-                }
+            for (int i = 0; i < TM; ++i)
 #pragma unroll
                 for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
+            if (!next_unit<BM, BN, LAYOUT>(p, cur.u + gridDim.x, cur)) break;
+            c = cur.c0;
+        } else {
+            ++c;
         }
-        if (!have_next) break;
-        if (last) cur_sb_blk0 = sb_blk0;
-        t = nt;
-        cur = nxt;
-        c = nc;
-        s ^= 1;
+        sq = sn;
+        si = si + 1 == NS ? 0 : si + 1;
         cr = nr;
+    }
+    // Copies issued past the end of the stream (repeats of the last chunk) may still be in
+    // flight; the workgroup's LDS must not be released under them.
+    wait_loads<0>();
+}
+
+// Split-K reduction: for every tile with valid rows, the FP32 partials of its K splits
+// are added in split order 0, 1, ..., S-1 (the same order whatever order the splits
+// finished in, so results are reproducible), rounded to BF16 and stored at valid rows
+// and columns exactly as the GEMM kernel's own epilogue would.
+template <int BM, int BN, int WM, int WN, int LAYOUT>
+__global__ void __launch_bounds__(64 * WM * WN) fp8bs_splitk_reduce(GemmParams p) {
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int TM = WTM / 16, TN = WTN / 16;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+    const int lj = lane & 15, kq = lane >> 4;
+    const int flip = (TM > 1) ? (lj >> 3) : 0;
+    for (int t = blockIdx.x; t < p.tiles; t += gridDim.x) {
+        Tile tl;
+        if (!tile_at<BM, BN, LAYOUT>(p, t, tl)) continue;
+        f32x4 acc[TM][TN];
+        const f32x4* ws = (const f32x4*)(p.ws + (int64_t)t * p.splits * (BM * BN));
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) acc[i][j] = ws[partial_index<TM, TN>(wave, i, j, lane)];
+        for (int s = 1; s < p.splits; ++s) {
+            const f32x4* wss = ws + (int64_t)s * (BM * BN / 4);
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j) acc[i][j] += wss[partial_index<TM, TN>(wave, i, j, lane)];
+        }
+        store_tile<TM, TN, WTM, WTN, LAYOUT>(p, tl, acc, wm, wn, lj, kq, flip);
     }
 }
 
@@ -480,13 +570,17 @@ typedef void (*KernelFn)(GemmParams);
 
 struct InstanceEntry {
     KernelFn fn[3];
+    KernelFn reduce[3];
     int threads;
 };
 
-#define FP8BS_INSTANCE(BM, BN, WM, WN, OCC, CNS, TNS)                         \
-    {{fp8bs_gemm_kernel<BM, BN, WM, WN, kDense>,                              \
-      fp8bs_gemm_kernel<BM, BN, WM, WN, kContiguous>,                         \
-      fp8bs_gemm_kernel<BM, BN, WM, WN, kMasked>},                            \
+#define FP8BS_INSTANCE(BM, BN, WM, WN, NS, OCC, CNS, TNS)                     \
+    {{fp8bs_gemm_kernel<BM, BN, WM, WN, NS, kDense>,                          \
+      fp8bs_gemm_kernel<BM, BN, WM, WN, NS, kContiguous>,                     \
+      fp8bs_gemm_kernel<BM, BN, WM, WN, NS, kMasked>},                        \
+     {fp8bs_splitk_reduce<BM, BN, WM, WN, kDense>,                            \
+      fp8bs_splitk_reduce<BM, BN, WM, WN, kContiguous>,                       \
+      fp8bs_splitk_reduce<BM, BN, WM, WN, kMasked>},                          \
      64 * (WM) * (WN)},
 const InstanceEntry kEntries[] = {
 #include "fp8bs_instances.inc"
@@ -501,7 +595,11 @@ int launch_instance(const Plan& plan, int layout, const GemmParams& p, hipStream
     const InstanceEntry& e = kEntries[plan.instance];
     GemmParams args = p;
     void* argv[] = {&args};
-    return (int)hipLaunchKernel((const void*)e.fn[layout], dim3((unsigned)plan.grid),
+    hipError_t err = hipLaunchKernel((const void*)e.fn[layout], dim3((unsigned)plan.grid),
+                                     dim3(e.threads), argv, 0, stream);
+    if (err != hipSuccess || p.splits == 1) return (int)err;
+    // one workgroup per tile (tiles without valid rows return at once)
+    return (int)hipLaunchKernel((const void*)e.reduce[layout], dim3((unsigned)p.tiles),
                                 dim3(e.threads), argv, 0, stream);
 }
 

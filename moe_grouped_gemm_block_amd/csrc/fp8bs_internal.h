@@ -11,9 +11,11 @@ enum Layout : int { kDense = 0, kContiguous = 1, kMasked = 2 };
 
 // Shape of one compiled kernel instance: an output tile of block_m x block_n
 // computed by waves_m x waves_n wavefronts (64 lanes each), each owning a
-// (block_m / waves_m) x (block_n / waves_n) sub-tile made of 16x16 MFMA tiles.
+// (block_m / waves_m) x (block_n / waves_n) sub-tile made of 16x16 MFMA tiles,
+// with a ring of `stages` LDS stages (one 128-K chunk each) in flight.
 struct InstanceShape {
     int block_m, block_n, waves_m, waves_n;
+    int stages;
     int wg_per_cu;       // workgroups per CU the launch assumes (LDS / register bound)
     int lds_bytes;
     int chunk_ns;        // cost model: CU time per 128-K chunk of one tile
@@ -25,7 +27,7 @@ struct InstanceShape {
 constexpr int stage_bytes(int block_m, int block_n) {
     return (block_m + block_n) * 128 + block_m * 4 + 256;
 }
-constexpr int kStages = 2;
+constexpr int kLdsBytesPerCu = 160 * 1024;
 
 // The instance table (defined next to the kernels, read by the planner).
 extern const InstanceShape kInstances[];
@@ -48,6 +50,9 @@ struct GemmParams {
     int n_blocks;       // ceil(n / block_n)
     int tiles;          // (num_groups for masked) x m_blocks x n_blocks
     int raster;         // m-blocks per raster group
+    int splits;         // K splits per tile (1: no workspace use)
+    int units;          // tiles x splits
+    float* ws;          // splits > 1: FP32 partial tiles, [tile][split][block_m*block_n]
 };
 
 struct Plan {
@@ -56,16 +61,26 @@ struct Plan {
     int64_t tiles;
     int64_t grid;
     int raster;
+    int splits;
+    int64_t workspace_bytes;    // bytes of workspace the launch uses (0 when splits == 1)
 };
 
-// Host planner: deterministic choice of an instance and launch shape.
+// Workspace bytes a launch of `shape` with `splits` K splits needs.
+int64_t split_workspace_bytes(const InstanceShape& shape, int64_t tiles, int splits);
+
+// Host planner: deterministic choice of an instance, a K split count (only when the
+// caller offers at least that much workspace) and launch shape.
 // Returns FP8BS_OK or an error status.  No device access.
 int plan_request(int layout, int64_t m, int n, int k, int num_groups, int expected_m,
-                 int num_cus, Plan* out);
+                 int num_cus, int64_t workspace_bytes, Plan* out);
 
-// Launch shape for a given instance (used when an instance is pinned).
-int plan_instance(int instance, int layout, int64_t m, int n, int num_groups, int num_cus,
-                  Plan* out);
+// Launch shape for a given instance and split count (used when either is pinned;
+// splits < 1 picks the best split count for the instance within the workspace).
+int plan_instance(int instance, int splits, int layout, int64_t m, int n, int k, int num_groups,
+                  int expected_m, int num_cus, int64_t workspace_bytes, Plan* out);
+
+// Copies a plan into the public struct.
+void export_plan(const Plan& p, fp8bs_plan* out);
 
 // Validates sizes for an entry point (FP8BS_OK or FP8BS_ERR_SHAPE).
 int validate_sizes(int layout, int64_t m, int n, int k, int num_groups);

@@ -16,8 +16,8 @@
 
 namespace fp8bs {
 
-#define FP8BS_INSTANCE(BM, BN, WM, WN, OCC, CNS, TNS) \
-    {BM, BN, WM, WN, OCC, kStages * stage_bytes(BM, BN), CNS, TNS},
+#define FP8BS_INSTANCE(BM, BN, WM, WN, NS, OCC, CNS, TNS) \
+    {BM, BN, WM, WN, NS, OCC, NS * stage_bytes(BM, BN), CNS, TNS},
 const InstanceShape kInstances[] = {
 #include "fp8bs_instances.inc"
 };
@@ -40,20 +40,108 @@ int validate_sizes(int layout, int64_t m, int n, int k, int num_groups) {
     return FP8BS_OK;
 }
 
-// Cost model (nanoseconds).  A CU works through ceil(tiles / CUs) tiles, each costing
-// chunks * chunk_ns + tile_ns (measured per instance); the whole chip cannot beat
-// reading every operand byte once from HBM; and a launch that leaves CUs idle keeps
-// fewer loads in flight, so under-fill is penalised.
-static const double kHbmBytesPerNs = 8.0e12 / 1.0e9;
+int64_t split_workspace_bytes(const InstanceShape& shape, int64_t tiles, int splits) {
+    if (splits <= 1) return 0;
+    return tiles * splits * (int64_t)shape.block_m * shape.block_n * 4;
+}
 
-static void fill_launch(int i, int layout, int64_t m, int n, int num_groups, int num_cus,
-                        Plan* out) {
+// Cost model (nanoseconds).  The persistent grid deals work units (tile, K split)
+// round-robin, so a CU works through ceil(units / CUs) units, each costing
+// chunks_per_unit * chunk_ns + tile_ns (measured per instance); the whole chip cannot beat
+// reading every operand byte once from HBM (plus the FP32 partials of a split launch,
+// written once and read once); a split launch adds the reduction kernel; and a launch
+// that leaves CUs idle keeps fewer loads in flight, so under-fill is penalised.
+static const double kHbmBytesPerNs = 8.0e12 / 1.0e9;
+static const double kReduceFixedNs = 2500.0;         // second launch and its tail
+static const double kReduceBytesPerNs = 4.0e12 / 1.0e9;
+static const int kMaxSplits = 16;
+
+namespace {
+
+struct Request {
+    int layout;
+    int64_t m;
+    int n, k, G;
+    int64_t eff_rows;    // rows per group the estimate assumes
+    int64_t spread;      // masked: masked_m assumed uniform over 1 .. spread (0: off)
+    int num_cus;
+    int64_t workspace_bytes;
+};
+
+Request make_request(int layout, int64_t m, int n, int k, int num_groups, int expected_m,
+                     int num_cus, int64_t workspace_bytes) {
+    Request r;
+    r.layout = layout;
+    r.m = m;
+    r.n = n;
+    r.k = k;
+    r.G = layout == kDense ? 1 : num_groups;
+    r.eff_rows = m;
+    if (layout == kMasked && expected_m > 0 && expected_m < m) r.eff_rows = expected_m;
+    // masked: expected_m is read as the mean of masked_m, spread uniformly over
+    // 1 .. min(2 * expected_m, max_m); a group costs E[ceil(masked_m / block_m)] m-blocks
+    r.spread = layout == kMasked && expected_m > 0
+                   ? (2 * (int64_t)expected_m < m ? 2 * (int64_t)expected_m : m)
+                   : 0;
+    r.num_cus = num_cus;
+    r.workspace_bytes = workspace_bytes < 0 ? 0 : workspace_bytes;
+    return r;
+}
+
+int64_t tile_count(const Request& r, const InstanceShape& s) {
+    const int64_t m_blocks = (r.m + s.block_m - 1) / s.block_m;
+    const int64_t n_blocks = ((int64_t)r.n + s.block_n - 1) / s.block_n;
+    return (r.layout == kMasked ? r.G : 1) * m_blocks * n_blocks;
+}
+
+bool instance_fits(const Request& r, const InstanceShape& s) {
+    // a contiguous-layout tile must not straddle two 128-row expert blocks
+    return !(r.layout == kContiguous && 128 % s.block_m != 0);
+}
+
+// Estimated time of instance s with `splits` K splits; < 0 when infeasible.
+double estimate(const Request& r, const InstanceShape& s, int splits) {
+    const int kchunks = r.k / 128;
+    if (splits < 1 || splits > kchunks) return -1.0;
+    const int64_t tiles = tile_count(r, s);
+    // unit indices (and unit + grid) stay well inside int
+    if (tiles * splits > 0x7f000000) return -1.0;
+    if (split_workspace_bytes(s, tiles, splits) > r.workspace_bytes) return -1.0;
+    const int64_t n_blocks = ((int64_t)r.n + s.block_n - 1) / s.block_n;
+    double eff_m_blocks = (double)((r.eff_rows + s.block_m - 1) / s.block_m);
+    if (r.spread > 0) {                          // mean of ceil(x / block_m), x = 1 .. spread
+        const int64_t full = r.spread / s.block_m, rest = r.spread % s.block_m;
+        double sum = (double)s.block_m * full * (full + 1) / 2.0;
+        sum += (double)rest * (full + 1);
+        eff_m_blocks = sum / r.spread;
+    }
+    const double eff_tiles = (r.layout == kMasked ? r.G : 1) * eff_m_blocks * n_blocks;
+    const int64_t units = tiles * splits;
+    const int64_t per_cu = (units + r.num_cus - 1) / r.num_cus;
+    const int64_t chunks_per_unit = (kchunks + splits - 1) / splits;
+    double t = per_cu * (chunks_per_unit * (double)s.chunk_ns + s.tile_ns);
+    double bytes = (double)r.G * r.eff_rows * r.k + (double)r.G * r.n * r.k +
+                   (double)r.G * r.eff_rows * r.n * 2;
+    const double partial_bytes = splits > 1 ? eff_tiles * splits * s.block_m * s.block_n * 4.0 : 0.0;
+    bytes += 2.0 * partial_bytes;
+    const double t_hbm = bytes / kHbmBytesPerNs;
+    if (t < t_hbm) t = t_hbm;
+    const double eff_units = ceil(eff_tiles * splits - 1e-9);
+    const double fill = (eff_units < r.num_cus ? eff_units : (double)r.num_cus) / r.num_cus;
+    t *= 1.0 + 0.1 * (1.0 - fill);
+    if (splits > 1)
+        t += kReduceFixedNs +
+             (partial_bytes + (double)r.G * r.eff_rows * r.n * 2) / kReduceBytesPerNs;
+    return t;
+}
+
+void fill_launch(int i, const Request& r, int splits, Plan* out) {
     const InstanceShape& s = kInstances[i];
-    const int64_t m_blocks = (m + s.block_m - 1) / s.block_m;
-    const int64_t n_blocks = ((int64_t)n + s.block_n - 1) / s.block_n;
-    const int64_t tiles = (layout == kMasked ? num_groups : 1) * m_blocks * n_blocks;
-    const int64_t slots = (int64_t)num_cus * s.wg_per_cu;
-    int64_t grid = tiles < slots ? tiles : slots;
+    const int64_t m_blocks = (r.m + s.block_m - 1) / s.block_m;
+    const int64_t tiles = tile_count(r, s);
+    const int64_t slots = (int64_t)r.num_cus * s.wg_per_cu;
+    const int64_t units = tiles * splits;
+    int64_t grid = units < slots ? units : slots;
     if (grid < 1) grid = 1;
     out->instance = i;
     out->shape = s;
@@ -61,82 +149,65 @@ static void fill_launch(int i, int layout, int64_t m, int n, int num_groups, int
     out->grid = grid;
     const int64_t raster = m_blocks < 8 ? m_blocks : 8;
     out->raster = raster < 1 ? 1 : (int)raster;
+    out->splits = splits;
+    out->workspace_bytes = split_workspace_bytes(s, tiles, splits);
 }
 
-int plan_instance(int instance, int layout, int64_t m, int n, int num_groups, int num_cus,
-                  Plan* out) {
+}  // namespace
+
+int plan_instance(int instance, int splits, int layout, int64_t m, int n, int k, int num_groups,
+                  int expected_m, int num_cus, int64_t workspace_bytes, Plan* out) {
     if (instance < 0 || instance >= kNumInstances || num_cus < 1) return FP8BS_ERR_UNSUPPORTED;
+    const Request r = make_request(layout, m, n, k, num_groups, expected_m, num_cus, workspace_bytes);
     const InstanceShape& s = kInstances[instance];
-    if (layout == kContiguous && 128 % s.block_m != 0) return FP8BS_ERR_UNSUPPORTED;
-    const int64_t tiles = (layout == kMasked ? num_groups : 1) * ((m + s.block_m - 1) / s.block_m) *
-                          (((int64_t)n + s.block_n - 1) / s.block_n);
-    if (tiles > 0x7fffffff) return FP8BS_ERR_UNSUPPORTED;
-    fill_launch(instance, layout, m, n, layout == kMasked ? num_groups : 1, num_cus, out);
+    if (!instance_fits(r, s)) return FP8BS_ERR_UNSUPPORTED;
+    int best_s = -1;
+    if (splits >= 1) {
+        if (estimate(r, s, splits) < 0) return FP8BS_ERR_UNSUPPORTED;
+        best_s = splits;
+    } else {
+        double best_t = 0;
+        for (int sp = 1; sp <= kMaxSplits; ++sp) {
+            const double t = estimate(r, s, sp);
+            if (t >= 0 && (best_s < 0 || t < best_t * (1.0 - 1e-9))) {
+                best_s = sp;
+                best_t = t;
+            }
+        }
+        if (best_s < 0) return FP8BS_ERR_UNSUPPORTED;
+    }
+    fill_launch(instance, r, best_s, out);
     return FP8BS_OK;
 }
 
 int plan_request(int layout, int64_t m, int n, int k, int num_groups, int expected_m,
-                 int num_cus, Plan* out) {
+                 int num_cus, int64_t workspace_bytes, Plan* out) {
     int st = validate_sizes(layout, m, n, k, layout == kDense ? 1 : num_groups);
     if (st != FP8BS_OK) return st;
     if (num_cus < 1) return FP8BS_ERR_UNSUPPORTED;
-    const int G = layout == kDense ? 1 : num_groups;
-    int64_t eff_rows = m;                        // rows per group the estimate assumes
-    if (layout == kMasked && expected_m > 0 && expected_m < m) eff_rows = expected_m;
-    // masked: expected_m is read as the mean of masked_m, spread uniformly over
-    // 1 .. min(2 * expected_m, max_m); a group costs E[ceil(masked_m / block_m)] m-blocks
-    const int64_t spread = layout == kMasked && expected_m > 0
-                               ? (2 * (int64_t)expected_m < m ? 2 * (int64_t)expected_m : m)
-                               : 0;
+    const Request r = make_request(layout, m, n, k, num_groups, expected_m, num_cus, workspace_bytes);
     double best_t = 0;
-    int best = -1;
-    Plan best_plan = {};
+    int best = -1, best_s = 1;
     for (int i = 0; i < kNumInstances; ++i) {
         const InstanceShape& s = kInstances[i];
-        if (layout == kContiguous && 128 % s.block_m != 0) continue;
-        const int64_t m_blocks = (m + s.block_m - 1) / s.block_m;
-        const int64_t n_blocks = ((int64_t)n + s.block_n - 1) / s.block_n;
-        const int64_t tiles = (layout == kMasked ? G : 1) * m_blocks * n_blocks;
-        if (tiles > 0x7fffffff) continue;
-        double eff_m_blocks = (double)((eff_rows + s.block_m - 1) / s.block_m);
-        if (spread > 0) {                          // mean of ceil(x / block_m), x = 1 .. spread
-            const int64_t full = spread / s.block_m, rest = spread % s.block_m;
-            double sum = (double)s.block_m * full * (full + 1) / 2.0;
-            sum += (double)rest * (full + 1);
-            eff_m_blocks = sum / spread;
-        }
-        const int64_t eff_tiles =
-            (int64_t)ceil((layout == kMasked ? G : 1) * eff_m_blocks * n_blocks - 1e-9);
-        // the schedule is static: tiles (skipped ones included) are dealt round-robin, so a
-        // CU may be handed ceil(tiles / CUs) tiles that all hold valid rows
-        const int64_t per_cu = (tiles + num_cus - 1) / num_cus;
-        const double bytes = (double)G * eff_rows * k + (double)G * n * k + (double)G * eff_rows * n * 2;
-        const double t_hbm = bytes / kHbmBytesPerNs;
-        double t = per_cu * ((k / 128) * (double)s.chunk_ns + s.tile_ns);
-        if (t < t_hbm) t = t_hbm;
-        const double fill = (double)(eff_tiles < num_cus ? eff_tiles : num_cus) / num_cus;
-        t *= 1.0 + 0.1 * (1.0 - fill);
-        if (best < 0 || t < best_t * (1.0 - 1e-9)) {
-            best = i;
-            best_t = t;
-            fill_launch(i, layout, m, n, G, num_cus, &best_plan);
+        if (!instance_fits(r, s)) continue;
+        for (int sp = 1; sp <= kMaxSplits; ++sp) {
+            const double t = estimate(r, s, sp);
+            if (t < 0) continue;
+            if (best < 0 || t < best_t * (1.0 - 1e-9)) {
+                best = i;
+                best_s = sp;
+                best_t = t;
+            }
         }
     }
     if (best < 0) return FP8BS_ERR_UNSUPPORTED;
-    *out = best_plan;
+    fill_launch(best, r, best_s, out);
     return FP8BS_OK;
 }
 
-}  // namespace fp8bs
-
-extern "C" int fp8bs_plan_query(int layout, int64_t m, int n, int k, int num_groups,
-                                int expected_m, int num_cus, fp8bs_plan* out) {
-    if (!out) return FP8BS_ERR_POINTER;
-    if (layout < 0 || layout > 2) return FP8BS_ERR_UNSUPPORTED;
-    fp8bs::Plan p;
-    int st = fp8bs::plan_request(layout, m, n, k, layout == 0 ? 1 : num_groups, expected_m,
-                                 num_cus, &p);
-    if (st != FP8BS_OK) return st;
+void export_plan(const Plan& p, fp8bs_plan* out) {
+    *out = fp8bs_plan{};
     out->block_m = p.shape.block_m;
     out->block_n = p.shape.block_n;
     out->waves_m = p.shape.waves_m;
@@ -144,10 +215,27 @@ extern "C" int fp8bs_plan_query(int layout, int64_t m, int n, int k, int num_gro
     out->threads = 64 * p.shape.waves_m * p.shape.waves_n;
     out->lds_bytes = p.shape.lds_bytes;
     out->wg_per_cu = p.shape.wg_per_cu;
+    out->stages = p.shape.stages;
     out->tiles = p.tiles;
     out->grid = p.grid;
     out->raster = p.raster;
     out->instance = p.instance;
+    out->splits = p.splits;
+    out->workspace_bytes = p.workspace_bytes;
+}
+
+}  // namespace fp8bs
+
+extern "C" int fp8bs_plan_query(int layout, int64_t m, int n, int k, int num_groups,
+                                int expected_m, int num_cus, int64_t workspace_bytes,
+                                fp8bs_plan* out) {
+    if (!out) return FP8BS_ERR_POINTER;
+    if (layout < 0 || layout > 2) return FP8BS_ERR_UNSUPPORTED;
+    fp8bs::Plan p;
+    int st = fp8bs::plan_request(layout, m, n, k, layout == 0 ? 1 : num_groups, expected_m,
+                                 num_cus, workspace_bytes, &p);
+    if (st != FP8BS_OK) return st;
+    fp8bs::export_plan(p, out);
     return FP8BS_OK;
 }
 
@@ -165,16 +253,11 @@ extern "C" int fp8bs_num_instances(void) { return fp8bs::kNumInstances; }
 extern "C" int fp8bs_instance_info(int i, fp8bs_plan* out) {
     if (!out) return FP8BS_ERR_POINTER;
     if (i < 0 || i >= fp8bs::kNumInstances) return FP8BS_ERR_UNSUPPORTED;
-    const fp8bs::InstanceShape& s = fp8bs::kInstances[i];
-    *out = fp8bs_plan{};
-    out->block_m = s.block_m;
-    out->block_n = s.block_n;
-    out->waves_m = s.waves_m;
-    out->waves_n = s.waves_n;
-    out->threads = 64 * s.waves_m * s.waves_n;
-    out->lds_bytes = s.lds_bytes;
-    out->wg_per_cu = s.wg_per_cu;
-    out->instance = i;
+    fp8bs::Plan p = {};
+    p.instance = i;
+    p.shape = fp8bs::kInstances[i];
+    p.splits = 1;
+    fp8bs::export_plan(p, out);
     return FP8BS_OK;
 }
 
@@ -184,7 +267,8 @@ extern "C" const char* fp8bs_status_string(int status) {
         case FP8BS_ERR_SHAPE: return "invalid shape (K must be a positive multiple of 128, "
                                      "m_total a multiple of 128, sizes positive)";
         case FP8BS_ERR_POINTER: return "NULL or misaligned (not 16-byte) pointer";
-        case FP8BS_ERR_UNSUPPORTED: return "no compiled kernel instance covers the request";
+        case FP8BS_ERR_UNSUPPORTED: return "no compiled kernel instance covers the request "
+                                           "(or a pinned instance / split count does not fit it)";
         case FP8BS_ERR_HIP: return "HIP runtime error";
         default: return "unknown status";
     }

@@ -63,16 +63,22 @@ class DeviceProblem:
     def reset(self):
         self.d.fill_(SENTINEL)          # 0x7FC1 fits in int16
 
-    def run(self, stream=None):
+    def run(self, stream=None, workspace=True):
+        """One call through the C ABI: the workspace (split-K capable) entry point by
+        default, the workspace-free one with workspace=False."""
         p = self.p
         if p.kind == "dense":
-            fp8bs.dense_nt(self.a, self.sfa, self.b, self.sfb, self.d, stream=stream)
+            if workspace:
+                fp8bs.fp8bs_dense_nt_ws(self.a, self.sfa, self.b, self.sfb, self.d, stream=stream)
+            else:
+                fp8bs.fp8bs_dense_nt(self.a, self.sfa, self.b, self.sfb, self.d, stream=stream)
         elif p.kind == "contiguous":
-            fp8bs.grouped_contiguous_nt(self.a, self.sfa, self.b, self.sfb, self.d, self.layout,
-                                        stream=stream)
+            f = fp8bs.fp8bs_grouped_contiguous_nt_ws if workspace else fp8bs.fp8bs_grouped_contiguous_nt
+            f(self.a, self.sfa, self.b, self.sfb, self.d, self.layout, stream=stream)
         else:
-            fp8bs.grouped_masked_nt(self.a, self.sfa, self.b, self.sfb, self.d, self.masked_m,
-                                    expected_m=p.expected_m, stream=stream)
+            f = fp8bs.fp8bs_grouped_masked_nt_ws if workspace else fp8bs.fp8bs_grouped_masked_nt
+            f(self.a, self.sfa, self.b, self.sfb, self.d, self.masked_m, expected_m=p.expected_m,
+              stream=stream)
 
     def result(self) -> np.ndarray:
         torch.cuda.synchronize()

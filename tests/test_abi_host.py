@@ -146,3 +146,61 @@ def test_cu_cap_and_forced_instance_setters():
     assert fp8bs.force_instance(-1) == 0
     with pytest.raises(ValueError):
         fp8bs.force_instance(10 ** 6)
+
+
+def test_split_k_plans_respect_the_workspace():
+    big = 1 << 40
+    for fam in range(5):
+        for d in synth.workload_shapes(fam):
+            layout = {"dense": 0, "contiguous": 1, "masked": 2}[d["kind"]]
+            m = d.get("M", 0) if layout == 0 else (33152 if layout == 1 else d["max_m"])
+            g = d.get("G", 1)
+            q0 = fp8bs.plan_query(layout, m, d["N"], d["K"], g, d.get("expected_m", 0), 256, 0)
+            assert q0["splits"] == 1 and q0["workspace_bytes"] == 0
+            q = fp8bs.plan_query(layout, m, d["N"], d["K"], g, d.get("expected_m", 0), 256, big)
+            assert 1 <= q["splits"] <= d["K"] // 128
+            assert 1 <= q["grid"] <= q["tiles"] * q["splits"]
+            want = 0 if q["splits"] == 1 else q["tiles"] * q["splits"] * q["block_m"] * q["block_n"] * 4
+            assert q["workspace_bytes"] == want
+            if want:
+                # any smaller workspace yields a plan that fits in it
+                q2 = fp8bs.plan_query(layout, m, d["N"], d["K"], g, d.get("expected_m", 0), 256,
+                                      want - 1)
+                assert q2["workspace_bytes"] <= want - 1
+
+
+def test_split_k_fills_the_cus_for_decode():
+    # M = 64 decode against a 7168x7168 weight: 64-row tiles alone give at most 112 units
+    q = fp8bs.plan_query(fp8bs.LAYOUT_DENSE, 64, 7168, 7168, num_cus=256, workspace_bytes=1 << 32)
+    assert q["splits"] > 1
+    assert q["tiles"] * q["splits"] >= 0.75 * 256
+
+
+def test_workspace_entry_points_validate_before_launching():
+    lib = fp8bs._load()
+    f = _Fake().ptr
+    assert lib.fp8bs_dense_nt_ws(f, f, f, f, f, 128, 2112, 100, f, 1024, None) == ERR_SHAPE
+    assert lib.fp8bs_dense_nt_ws(f, f, f, f, f, 128, 16, 128, f + 4, 1024, None) == ERR_POINTER
+    assert lib.fp8bs_dense_nt_ws(f, f, f, f, f, 128, 16, 128, None, 1024, None) == ERR_POINTER
+    assert lib.fp8bs_grouped_contiguous_nt_ws(f, f, f, f, f, f, 100, 16, 128, 2, f, 0, None) \
+        == ERR_SHAPE
+    assert lib.fp8bs_grouped_masked_nt_ws(f, f, f, f, f, f, 0, 64, 0, 16, 128, f, 0, None) == ERR_SHAPE
+    assert lib.fp8bs_grouped_masked_nt_ws(f, f, f, f, f, None, 2, 64, 0, 16, 128, f, 0, None) \
+        == ERR_POINTER
+    assert lib.fp8bs_dense_nt_ws(f, f, f, f, f, 0, 16, 128, None, 0, None) == OK
+    assert lib.fp8bs_grouped_masked_nt_ws(f, f, f, f, f, f, 2, 0, 0, 16, 128, None, 0, None) == OK
+
+
+def test_forced_splits_setter():
+    assert fp8bs.force_splits(3) == 0
+    assert fp8bs.force_splits(0) == 3
+    assert fp8bs._load().fp8bs_force_splits(-1) == -1
+    with pytest.raises(ValueError):
+        fp8bs.force_splits(-2)
+
+
+def test_workspace_size_reports_errors_as_negated_status():
+    lib = fp8bs._load()
+    assert lib.fp8bs_workspace_size(0, 64, 256, 100, 1, 0) == -ERR_SHAPE
+    assert lib.fp8bs_workspace_size(7, 64, 256, 128, 1, 0) == -ERR_UNSUPPORTED
+    assert lib.fp8bs_workspace_size(0, 0, 256, 128, 1, 0) == 0

@@ -26,14 +26,16 @@ def _say(msg):
 @pytest.fixture(autouse=True)
 def _planner_choice():
     fp8bs.force_instance(-1)
+    fp8bs.force_splits(0)
     yield
     fp8bs.force_instance(-1)
+    fp8bs.force_splits(0)
 
 
-def _run_and_check(p, what):
-    _say(f"[gpu] {what}: {p.kind} M={p.M} N={p.N} K={p.K} G={p.G}")
+def _run_and_check(p, what, workspace=True):
+    _say(f"[gpu] {what}: {p.kind} M={p.M} N={p.N} K={p.K} G={p.G} workspace={workspace}")
     dp = DeviceProblem(p)
-    dp.run()
+    dp.run(workspace=workspace)
     gpu = dp.result()
     ref = oracle_full(p)
     return check_full(p, gpu, ref, what)
@@ -48,14 +50,14 @@ def _instances(layout):
     return out
 
 
-N_INST = 11
+N_INST = len(fp8bs.instances())
 
 
 @pytest.mark.parametrize("inst", range(N_INST))
 def test_dense_every_instance(inst):
     fp8bs.force_instance(inst)
     p = synth.make_dense(300, 500, 512, seed=11 + inst)
-    _run_and_check(p, f"dense inst {inst}")
+    _run_and_check(p, f"dense inst {inst}", workspace=False)
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 128), (5, 2112, 256), (129, 129, 128), (64, 7168, 384),
@@ -71,7 +73,7 @@ def test_contiguous_every_instance(inst):
         pytest.skip("block_m does not divide the 128-row alignment")
     fp8bs.force_instance(inst)
     p = synth.make_contiguous(4, 300, 384, seed=31 + inst, counts=[200, 0, 1, 129])
-    _run_and_check(p, f"contiguous inst {inst}")
+    _run_and_check(p, f"contiguous inst {inst}", workspace=False)
 
 
 def test_contiguous_planner_multinomial():
@@ -83,7 +85,7 @@ def test_contiguous_planner_multinomial():
 def test_masked_every_instance(inst):
     fp8bs.force_instance(inst)
     p = synth.make_masked(5, 200, 300, 384, seed=51 + inst, masked_m=[0, 200, 1, 77, 129])
-    _run_and_check(p, f"masked inst {inst}")
+    _run_and_check(p, f"masked inst {inst}", workspace=False)
 
 
 def test_masked_clamps_out_of_range_counts():
@@ -94,6 +96,100 @@ def test_masked_clamps_out_of_range_counts():
 def test_masked_planner_expected_m():
     p = synth.make_masked(16, 256, 384, 512, seed=62, expected_m=128)
     _run_and_check(p, "masked expected_m")
+
+
+# ---- split-K (workspace entry points) --------------------------------------------
+
+@pytest.mark.parametrize("inst", range(N_INST))
+@pytest.mark.parametrize("splits", [2, 3])
+def test_dense_split_k_every_instance(inst, splits):
+    """K = 5 chunks: 2 splits give 2 + 3 chunks, 3 splits 1 + 2 + 2."""
+    fp8bs.force_instance(inst)
+    fp8bs.force_splits(splits)
+    p = synth.make_dense(200, 300, 640, seed=81 + inst)
+    _run_and_check(p, f"dense inst {inst} splits {splits}")
+
+
+@pytest.mark.parametrize("inst", range(N_INST))
+def test_contiguous_split_k_every_instance(inst):
+    if inst not in _instances(fp8bs.LAYOUT_CONTIGUOUS):
+        pytest.skip("block_m does not divide the 128-row alignment")
+    fp8bs.force_instance(inst)
+    fp8bs.force_splits(3)
+    p = synth.make_contiguous(4, 300, 768, seed=91 + inst, counts=[200, 0, 1, 129])
+    _run_and_check(p, f"contiguous inst {inst} splits 3")
+
+
+@pytest.mark.parametrize("inst", range(N_INST))
+def test_masked_split_k_every_instance(inst):
+    fp8bs.force_instance(inst)
+    fp8bs.force_splits(4)
+    p = synth.make_masked(5, 200, 300, 768, seed=101 + inst, masked_m=[0, 200, 1, 77, 129])
+    _run_and_check(p, f"masked inst {inst} splits 4")
+
+
+def test_split_k_one_chunk_per_unit():
+    fp8bs.force_splits(8)
+    p = synth.make_dense(70, 1000, 1024, seed=111)
+    _run_and_check(p, "dense splits 8 of 8 chunks")
+
+
+def test_split_k_more_splits_than_chunks_is_refused():
+    fp8bs.force_splits(3)
+    p = synth.make_dense(64, 256, 256, seed=112)
+    dp = DeviceProblem(p)
+    with pytest.raises(fp8bs.FP8BSError):
+        dp.run()
+
+
+def test_split_k_planner_decode_shape():
+    """The planner's own choice for a decode-sized dense GEMM (it splits K when that
+    fills the machine) against the oracle."""
+    p = synth.make_dense(64, 2048, 7168, seed=113)
+    _say(fp8bs.describe_config(fp8bs.LAYOUT_DENSE, 64, 2048, 7168))
+    _run_and_check(p, "dense decode planner")
+
+
+def test_split_k_deterministic_and_close_to_unsplit():
+    p = synth.make_dense(96, 700, 2048, seed=114)
+    ref = oracle_full(p)
+    dp = DeviceProblem(p)
+    fp8bs.force_splits(5)
+    dp.run()
+    d0 = dp.result()
+    check_full(p, d0, ref, "splits 5")
+    dp.reset()
+    dp.run()
+    assert np.array_equal(dp.result(), d0), "split-K results differ between runs"
+    dp.reset()
+    dp.run(workspace=False)
+    d1 = dp.result()
+    check_full(p, d1, ref, "no split")
+    # the two association orders agree with each other to the same bar
+    check_values(d0, d1, "splits 5 against no split")
+
+
+def test_split_k_reuses_a_caller_workspace():
+    p = synth.make_dense(64, 512, 1024, seed=115)
+    dp = DeviceProblem(p)
+    fp8bs.force_splits(4)
+    ws = torch.full((64 * 1024 * 1024,), 0xFF, dtype=torch.uint8, device="cuda")   # NaN bytes
+    for _ in range(2):
+        dp.reset()
+        fp8bs.fp8bs_dense_nt_ws(dp.a, dp.sfa, dp.b, dp.sfb, dp.d, workspace=ws)
+        check_full(p, dp.result(), oracle_full(p), "caller workspace")
+
+
+def test_split_k_short_workspace_is_refused_when_pinned():
+    p = synth.make_dense(64, 512, 1024, seed=116)
+    dp = DeviceProblem(p)
+    fp8bs.force_splits(4)
+    ws = torch.empty(1024, dtype=torch.uint8, device="cuda")
+    with pytest.raises(fp8bs.FP8BSError):
+        fp8bs.fp8bs_dense_nt_ws(dp.a, dp.sfa, dp.b, dp.sfb, dp.d, workspace=ws)
+    fp8bs.force_splits(0)                              # planner: falls back to what fits
+    fp8bs.fp8bs_dense_nt_ws(dp.a, dp.sfa, dp.b, dp.sfb, dp.d, workspace=ws)
+    check_full(p, dp.result(), oracle_full(p), "short workspace")
 
 
 # ---- closed forms, bit-exact on the GPU too ------------------------------------
@@ -143,6 +239,19 @@ def test_scale_shift_invariance_bit_exact():
     dp2 = DeviceProblem(p)
     dp2.run()
     assert np.array_equal(dp2.result(), d0)
+
+
+def test_constant_inputs_bit_exact_split_k():
+    M, N, K = 64, 300, 7168
+    p = synth.make_dense(M, N, K, seed=0)
+    p.A[:] = 0x38
+    p.B[:] = 0x38
+    p.SA[:] = 1.0
+    p.SB[:] = 1.0
+    fp8bs.force_splits(7)
+    dp = DeviceProblem(p)
+    dp.run()
+    assert np.all(dp.result() == 0x45E0)
 
 
 def test_run_to_run_determinism():
