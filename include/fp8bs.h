@@ -219,6 +219,8 @@ typedef struct {
     int instance;       /* index of the compiled kernel instance              */
     int splits;         /* K ranges per tile (1: no split, no workspace)      */
     int64_t workspace_bytes; /* workspace the plan uses (0 when splits == 1)  */
+    int kind;           /* 0: A and B tiles staged in LDS, persistent grid;
+                           1: B streamed into registers, one workgroup per unit */
 } fp8bs_plan;
 
 /*

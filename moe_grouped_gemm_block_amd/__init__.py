@@ -48,7 +48,8 @@ class _Plan(ctypes.Structure):
                 ("waves_n", ctypes.c_int), ("threads", ctypes.c_int), ("lds_bytes", ctypes.c_int),
                 ("wg_per_cu", ctypes.c_int), ("stages", ctypes.c_int), ("tiles", ctypes.c_int64),
                 ("grid", ctypes.c_int64), ("raster", ctypes.c_int), ("instance", ctypes.c_int),
-                ("splits", ctypes.c_int), ("workspace_bytes", ctypes.c_int64)]
+                ("splits", ctypes.c_int), ("workspace_bytes", ctypes.c_int64),
+                ("kind", ctypes.c_int)]
 
 
 def library_path() -> str:

@@ -48,10 +48,11 @@ void format_plan(const fp8bs::Plan& pl, int layout, int64_t m, int n, int k, int
                  int expected_m, int cus, char* buf, size_t len) {
     static const char* names[3] = {"dense", "contiguous", "masked"};
     snprintf(buf, len,
-             "fp8bs %s m=%lld n=%d k=%d groups=%d expected_m=%d cus=%d -> block %dx%d "
+             "fp8bs %s m=%lld n=%d k=%d groups=%d expected_m=%d cus=%d -> %s block %dx%d "
              "waves %dx%d threads %d stages %d lds %dB wg/cu %d tiles %lld splits %d "
              "workspace %lldB grid %lld raster %d instance %d",
-             names[layout], (long long)m, n, k, g, expected_m, cus, pl.shape.block_m,
+             names[layout], (long long)m, n, k, g, expected_m, cus,
+             pl.shape.kind == fp8bs::kStreamB ? "stream-B" : "staged", pl.shape.block_m,
              pl.shape.block_n, pl.shape.waves_m, pl.shape.waves_n,
              64 * pl.shape.waves_m * pl.shape.waves_n, pl.shape.stages, pl.shape.lds_bytes,
              pl.shape.wg_per_cu, (long long)pl.tiles, pl.splits, (long long)pl.workspace_bytes,

@@ -36,6 +36,8 @@
 // runs a contiguous range of that order.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "fp8bs_internal.h"
 
 namespace fp8bs {
@@ -78,6 +80,15 @@ __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "
 
 __device__ __forceinline__ void dma16(const void* src, LDS_AS void* dst_wave_base) {
     __builtin_amdgcn_global_load_lds((const GLOBAL_AS void*)src, dst_wave_base, 16, 0, 0);
+}
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I = B .. E-1.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -533,6 +544,238 @@ __global__ void __launch_bounds__(64 * WM * WN) fp8bs_gemm_kernel(GemmParams p) 
     wait_loads<0>();
 }
 
+// B-streaming kernel for few-row (decode) shapes.  Each workgroup computes one work
+// unit -- K split s of one block_m x block_n tile -- with its NW wavefronts side by side
+// along N: wavefront w owns columns n0 + w*WTN .. +WTN-1 and all block_m rows.
+//
+//   * B fragments are loaded from global memory straight into registers: every B byte
+//     is used by exactly one wavefront, so staging it in LDS buys nothing, and vector
+//     loads stream from HBM at a higher per-CU rate than direct-to-LDS copies.  Lane
+//     (j = l%16, quarter q = l/16) of the instruction's first operand takes 16-byte
+//     units q and q+4 of its B row's 128-byte chunk, so one load instruction covers 16
+//     rows x 64 contiguous bytes.  Loads run NS-1 chunks ahead, into a ring of NS
+//     register sets (the chunk loop is unrolled NS times so that ring slots are static).
+//   * The A tile, its scales and the B-scale values of each chunk go through an LDS ring
+//     of NS stages by direct-to-LDS copies, as in fp8bs_gemm_kernel; A fragments are
+//     read with the same K-unit assignment (q, q+4) as the B fragments, which keeps the
+//     chunk's dot products whole.
+//   * Products, promotion, epilogue and split-K partials are those of fp8bs_gemm_kernel
+//     with waves_m = 1, so fp8bs_splitk_reduce<BM, BN, 1, NW, LAYOUT> finishes a split.
+template <int BM, int BN, int NW, int NS, int LAYOUT>
+__global__ void __launch_bounds__(64 * NW) fp8bs_stream_kernel(GemmParams p) {
+    constexpr int WTN = BN / NW;                      // columns per wavefront
+    constexpr int TM = BM / 16, TN = WTN / 16;
+    static_assert(BM % 16 == 0 && WTN % 16 == 0 && NW >= 2, "tile shape");
+    static_assert(TM == 1 || TM == 2 || TM == 4 || TM == 8, "row blocks per wavefront");
+    // stage: A tile, 256 bytes of A scales (one per lane), 256 bytes of B scales
+    constexpr int SA_OFF = BM * 128, SB_OFF = SA_OFF + 256;
+    constexpr int STAGE = stream_stage_bytes(BM);
+    static_assert(BM <= 64 && STAGE == SB_OFF + 256, "stage layout");
+    static_assert(NS >= 2 && NS * STAGE <= kLdsBytesPerCu, "LDS ring");
+    constexpr int A_INS = BM / 8;                     // 1 KB (8 rows) per wavefront copy
+    constexpr int A_PER = (A_INS + NW - 1) / NW;
+    static_assert(BN / 128 + 2 <= 64, "B-scale blocks per tile");
+    constexpr int PD = NS - 1;                        // chunks in flight ahead
+    // per chunk and wavefront: 2 B loads per column block, A copies, one scale copy
+    constexpr int OPC = 2 * TN + A_PER + 1;
+    static_assert((PD - 1) * OPC <= 63, "vmcnt range");
+    constexpr bool UNIFORM_SB = (128 % WTN == 0) && (BN % 128 == 0 || 128 % BN == 0);
+
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int kchunks = p.k / 128;
+    const int K = p.k;
+    const int nsb = (p.n + 127) / 128;
+
+    Unit w;
+    // one unit per workgroup (the grid has one workgroup per unit): a tile without valid
+    // rows has nothing to do
+    if (!next_unit<BM, BN, LAYOUT>(p, logical_block_id(), w)) return;
+    const Tile tl = w.tl;
+    const int nch = w.c1 - w.c0;
+
+    // ---- A fragment addresses (as fp8bs_gemm_kernel with wm = 0; K units q and q+4) ----
+    const int lj = lane & 15;
+    const int kq = lane >> 4;
+    const int flip = (TM > 1) ? (lj >> 3) : 0;
+    int a_even[2], a_odd[2];
+    {
+        const int row0 = TM * lj;
+        const int key = a_key<TM>(row0);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int base = row0 * 128 + (((kq + 4 * h) ^ key) << 4);
+            a_even[h] = base + flip * 128;
+            a_odd[h] = base - flip * 128;
+        }
+    }
+    const int sa_rd = SA_OFF + TM * lj * 4;
+
+    // ---- B fragment sources: row n0 + wave*WTN + 16j + lj (clamped into the matrix) ----
+    const uint8_t* b_lane = p.b + (int64_t)tl.g * p.n * K + 16 * kq;
+    uint32_t b_row_off[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const int row = min(tl.n0 + wave * WTN + 16 * j + lj, p.n - 1);
+        b_row_off[j] = (uint32_t)row * (uint32_t)K;
+    }
+    auto issue_b = [&](int c, i32x8 (&dst)[TN]) {
+        const uint8_t* bc = b_lane + (int64_t)c * 128;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const i32x4 lo = *(const i32x4*)(bc + b_row_off[j]);
+            const i32x4 hi = *(const i32x4*)(bc + b_row_off[j] + 64);
+            dst[j] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+    };
+
+    // ---- A / scale copies of chunk c into stage s ----
+    const int cp_row = lane >> 3, cp_slot = lane & 7;
+    auto issue_a = [&](int c, int s) {
+        uint8_t* st = smem + s * STAGE;
+        const uint8_t* a_base = p.a + (LAYOUT == kMasked ? (int64_t)tl.g * p.m * K : (int64_t)0) +
+                                (int64_t)c * 128;
+#pragma unroll
+        for (int k = 0; k < A_PER; ++k) {
+            const int ins = min(wave + k * NW, A_INS - 1);   // extra copies repeat the last one
+            const int row = 8 * ins + cp_row;
+            const int grow = min(tl.m0 + row, tl.row_limit - 1);
+            const uint32_t off = (uint32_t)grow * (uint32_t)K + (uint32_t)((cp_slot ^ a_key<TM>(row)) << 4);
+            dma16(a_base + off, (LDS_AS void*)(st + ins * 1024));
+        }
+        // One 4-byte copy per lane and no lane masking, so that every wavefront issues the
+        // same number of memory operations per chunk on every path (the compiler counts
+        // them to place its waits for the B registers).  Lanes past the tile's rows or
+        // scale blocks copy a clamped in-range value into an unused LDS word.
+        if (wave == NW - 1) {
+            const uint8_t* sa_c = (const uint8_t*)(p.sfa +
+                (LAYOUT == kMasked ? (int64_t)tl.g * kchunks * p.sfa_ld : (int64_t)0) +
+                (int64_t)c * p.sfa_ld);
+            const uint32_t off = (uint32_t)min(tl.m0 + lane, p.sfa_ld - 1) * 4u;
+            __builtin_amdgcn_global_load_lds((const GLOBAL_AS void*)(sa_c + off),
+                                             (LDS_AS void*)(st + SA_OFF), 4, 0, 0);
+        } else {
+            const uint8_t* sb_c = (const uint8_t*)(p.sfb + (int64_t)tl.g * nsb * kchunks + c);
+            const uint32_t off = (uint32_t)min(tl.n0 / 128 + lane, nsb - 1) * (uint32_t)kchunks * 4u;
+            __builtin_amdgcn_global_load_lds((const GLOBAL_AS void*)(sb_c + off),
+                                             (LDS_AS void*)(st + SB_OFF), 4, 0, 0);
+        }
+    };
+
+    auto load_a = [&](const uint8_t* st, int i) {
+        const int* base = (i & 1) ? a_odd : a_even;
+        const i32x4 lo = *(const i32x4*)(st + base[0] + 128 * i);
+        const i32x4 hi = *(const i32x4*)(st + base[1] + 128 * i);
+        return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+
+    f32x4 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // multiply chunk in stage / ring slot `slot`
+    auto compute = [&](int slot, const i32x8 (&bf)[TN]) {
+        const uint8_t* st = smem + slot * STAGE;
+        float sa[TM];
+        {
+            const float* sap = (const float*)(st + sa_rd);
+#pragma unroll
+            for (int i = 0; i < TM; ++i) sa[i] = sap[i];
+            if (TM > 1) {
+#pragma unroll
+                for (int i = 0; i < TM; i += 2) {
+                    const float x = sa[i], y = sa[i + 1];
+                    sa[i] = flip ? y : x;
+                    sa[i + 1] = flip ? x : y;
+                }
+            }
+        }
+        float sb[UNIFORM_SB ? 1 : TN];
+        {
+            const float* sbl = (const float*)(st + SB_OFF);
+            const int blk0 = tl.n0 / 128;
+            if (UNIFORM_SB) {
+                sb[0] = sbl[min(tl.n0 + wave * WTN, p.n - 1) / 128 - blk0];
+            } else {
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    sb[j] = sbl[min(tl.n0 + wave * WTN + 16 * j, p.n - 1) / 128 - blk0];
+            }
+        }
+        i32x8 fa = load_a(st, 0);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            i32x8 fn;
+            if (i + 1 < TM) fn = load_a(st, i + 1);
+            const float s_i = sa[i];
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                __builtin_amdgcn_s_setprio(1);
+                const f32x4 part = mfma_e4m3(bf[j], fa);
+                __builtin_amdgcn_s_setprio(0);
+                acc[i][j] += part * (s_i * sb[UNIFORM_SB ? 0 : j]);
+            }
+            if (i + 1 < TM) fa = fn;
+        }
+    };
+
+    i32x8 breg[NS][TN];
+    // prologue: chunks 0 .. PD-1 (the last one repeated when the unit is shorter)
+#pragma unroll
+    for (int q = 0; q < PD; ++q) {
+        const int cq = w.c0 + min(q, nch - 1);
+        issue_a(cq, q);
+        issue_b(cq, breg[q]);
+    }
+    // Main loop over whole groups of NS chunks: straight-line code with the same memory
+    // operations on every path, so that the compiler's own waits for the B registers
+    // count exactly.  Chunk q sits in stage / register slot q % NS.
+    const int nfull = nch - nch % NS;
+    for (int base = 0; base < nfull; base += NS) {
+#pragma unroll
+        for (int ph = 0; ph < NS; ++ph) {
+            // chunk base+ph has landed for this wavefront; after the barrier, for every
+            // wavefront, and every wavefront is done with stage (ph + PD) % NS, which the
+            // chunk PD ahead reuses
+            wait_loads<(PD - 1) * OPC>();
+            block_barrier();
+            const int qi = min(base + ph + PD, nch - 1);
+            issue_a(w.c0 + qi, (ph + PD) % NS);
+            issue_b(w.c0 + qi, breg[(ph + PD) % NS]);
+            compute(ph, breg[ph]);
+        }
+    }
+    // Tail: the last nch % NS chunks are already in flight; nothing more is issued.
+    const int rest = nch - nfull;
+    static_for<0, NS - 1>([&](auto I) {
+        constexpr int ph = decltype(I)::value;
+        if (ph < rest) {
+            wait_loads<(PD - 1 - ph) * OPC>();
+            block_barrier();
+            compute(ph, breg[ph]);
+        }
+    });
+    wait_loads<0>();                                   // no copy may land after the exit
+
+    int el = lane;
+    asm volatile("" : "+v"(el));
+    if (p.splits == 1) {
+        const int elj = el & 15;
+        store_tile<TM, TN, BM, WTN, LAYOUT>(p, tl, acc, 0, wave, elj, el >> 4,
+                                            (TM > 1) ? (elj >> 3) : 0);
+    } else {
+        f32x4* ws = (f32x4*)(p.ws + ((int64_t)w.t * p.splits + w.s) * (BM * BN));
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) ws[partial_index<TM, TN>(wave, i, j, el)] = acc[i][j];
+    }
+}
+
 // Split-K reduction: for every tile with valid rows, the FP32 partials of its K splits
 // are added in split order 0, 1, ..., S-1 (the same order whatever order the splits
 // finished in, so results are reproducible), rounded to BF16 and stored at valid rows
@@ -574,10 +817,20 @@ struct InstanceEntry {
     int threads;
 };
 
-#define FP8BS_INSTANCE(BM, BN, WM, WN, NS, OCC, CNS, TNS)                     \
-    {{fp8bs_gemm_kernel<BM, BN, WM, WN, NS, kDense>,                          \
-      fp8bs_gemm_kernel<BM, BN, WM, WN, NS, kContiguous>,                     \
-      fp8bs_gemm_kernel<BM, BN, WM, WN, NS, kMasked>},                        \
+template <int KIND, int BM, int BN, int WM, int WN, int NS, int LAYOUT>
+constexpr KernelFn gemm_fn() {
+    if constexpr (KIND == kStreamB) {
+        static_assert(WM == 1, "B-streaming instances have one wavefront along M");
+        return fp8bs_stream_kernel<BM, BN, WN, NS, LAYOUT>;
+    } else {
+        return fp8bs_gemm_kernel<BM, BN, WM, WN, NS, LAYOUT>;
+    }
+}
+
+#define FP8BS_INSTANCE(KIND, BM, BN, WM, WN, NS, OCC, CNS, TNS, SCNS, STNS)    \
+    {{gemm_fn<KIND, BM, BN, WM, WN, NS, kDense>(),                            \
+      gemm_fn<KIND, BM, BN, WM, WN, NS, kContiguous>(),                       \
+      gemm_fn<KIND, BM, BN, WM, WN, NS, kMasked>()},                          \
      {fp8bs_splitk_reduce<BM, BN, WM, WN, kDense>,                            \
       fp8bs_splitk_reduce<BM, BN, WM, WN, kContiguous>,                       \
       fp8bs_splitk_reduce<BM, BN, WM, WN, kMasked>},                          \

@@ -9,23 +9,40 @@ namespace fp8bs {
 
 enum Layout : int { kDense = 0, kContiguous = 1, kMasked = 2 };
 
+// Kernel families.
+//   kStaged: A and B tiles both staged in LDS (direct-to-LDS copies), persistent grid;
+//            for shapes with enough rows that B tiles are shared by several wavefronts.
+//   kStreamB: B fragments loaded from global memory straight into registers (no LDS),
+//            A and the scales staged in LDS; one work unit per workgroup; for few-row
+//            (decode) shapes, where every B byte is used by one wavefront only and HBM
+//            bandwidth bounds the GEMM.
+enum Kind : int { kStaged = 0, kStreamB = 1 };
+
 // Shape of one compiled kernel instance: an output tile of block_m x block_n
 // computed by waves_m x waves_n wavefronts (64 lanes each), each owning a
 // (block_m / waves_m) x (block_n / waves_n) sub-tile made of 16x16 MFMA tiles,
 // with a ring of `stages` LDS stages (one 128-K chunk each) in flight.
 struct InstanceShape {
+    int kind;
     int block_m, block_n, waves_m, waves_n;
     int stages;
     int wg_per_cu;       // workgroups per CU the launch assumes (LDS / register bound)
     int lds_bytes;
     int chunk_ns;        // cost model: CU time per 128-K chunk of one tile
     int tile_ns;         // cost model: CU time per tile (prologue / epilogue)
+    int stream_chunk_ns; // the same two when the operands stream from HBM (few rows)
+    int stream_tile_ns;
 };
 
 // LDS bytes of one pipeline stage: the A tile, the B tile (128 K bytes per
 // row), the tile's block_m A scales and up to 64 B-scale values.
 constexpr int stage_bytes(int block_m, int block_n) {
     return (block_m + block_n) * 128 + block_m * 4 + 256;
+}
+// kStreamB: one stage holds the A tile, 256 bytes of A scales and 256 of B scales.
+constexpr int stream_stage_bytes(int block_m) { return block_m * 128 + 512; }
+constexpr int instance_lds_bytes(int kind, int block_m, int block_n, int stages) {
+    return stages * (kind == kStreamB ? stream_stage_bytes(block_m) : stage_bytes(block_m, block_n));
 }
 constexpr int kLdsBytesPerCu = 160 * 1024;
 

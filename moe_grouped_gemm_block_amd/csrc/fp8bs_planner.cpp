@@ -16,8 +16,8 @@
 
 namespace fp8bs {
 
-#define FP8BS_INSTANCE(BM, BN, WM, WN, NS, OCC, CNS, TNS) \
-    {BM, BN, WM, WN, NS, OCC, NS * stage_bytes(BM, BN), CNS, TNS},
+#define FP8BS_INSTANCE(KIND, BM, BN, WM, WN, NS, OCC, CNS, TNS, SCNS, STNS) \
+    {KIND, BM, BN, WM, WN, NS, OCC, instance_lds_bytes(KIND, BM, BN, NS), CNS, TNS, SCNS, STNS},
 const InstanceShape kInstances[] = {
 #include "fp8bs_instances.inc"
 };
@@ -55,6 +55,8 @@ static const double kHbmBytesPerNs = 8.0e12 / 1.0e9;
 static const double kReduceFixedNs = 2500.0;         // second launch and its tail
 static const double kReduceBytesPerNs = 4.0e12 / 1.0e9;
 static const int kMaxSplits = 16;
+static const double kRidgeFlopPerByte = 629.0;       // dense FP8 MFMA peak / HBM bandwidth
+static const double kStagedStreamingBias = 1.25;
 
 namespace {
 
@@ -119,7 +121,17 @@ double estimate(const Request& r, const InstanceShape& s, int splits) {
     const int64_t units = tiles * splits;
     const int64_t per_cu = (units + r.num_cus - 1) / r.num_cus;
     const int64_t chunks_per_unit = (kchunks + splits - 1) / splits;
-    double t = per_cu * (chunks_per_unit * (double)s.chunk_ns + s.tile_ns);
+    // Operands stream from HBM when a byte of A or B feeds fewer flops than the chip's
+    // ridge point (MFMA peak / HBM bandwidth): 2 x rows x N / (rows + N) flops per byte.
+    const bool streaming =
+        2.0 * (double)r.eff_rows * r.n / ((double)r.eff_rows + r.n) < kRidgeFlopPerByte;
+    const double c_ns = streaming ? s.stream_chunk_ns : s.chunk_ns;
+    const double t_ns = streaming ? s.stream_tile_ns : s.tile_ns;
+    double t = per_cu * (chunks_per_unit * c_ns + t_ns);
+    // The staged kernels' streaming-regime fit is loose (their direct-to-LDS copies slow
+    // down unevenly as they miss in L2); measured, they lose to the B-streaming kernel
+    // unless the model favours them by a wide margin.
+    if (streaming && s.kind == kStaged) t *= kStagedStreamingBias;
     double bytes = (double)r.G * r.eff_rows * r.k + (double)r.G * r.n * r.k +
                    (double)r.G * r.eff_rows * r.n * 2;
     const double partial_bytes = splits > 1 ? eff_tiles * splits * s.block_m * s.block_n * 4.0 : 0.0;
@@ -141,7 +153,8 @@ void fill_launch(int i, const Request& r, int splits, Plan* out) {
     const int64_t tiles = tile_count(r, s);
     const int64_t slots = (int64_t)r.num_cus * s.wg_per_cu;
     const int64_t units = tiles * splits;
-    int64_t grid = units < slots ? units : slots;
+    // kStaged: persistent grid; kStreamB: one workgroup per unit
+    int64_t grid = (s.kind == kStreamB || units < slots) ? units : slots;
     if (grid < 1) grid = 1;
     out->instance = i;
     out->shape = s;
@@ -222,6 +235,7 @@ void export_plan(const Plan& p, fp8bs_plan* out) {
     out->instance = p.instance;
     out->splits = p.splits;
     out->workspace_bytes = p.workspace_bytes;
+    out->kind = p.shape.kind;
 }
 
 }  // namespace fp8bs
