@@ -567,10 +567,11 @@ __global__ void __launch_bounds__(64 * NW) fp8bs_stream_kernel(GemmParams p) {
     constexpr int TM = BM / 16, TN = WTN / 16;
     static_assert(BM % 16 == 0 && WTN % 16 == 0 && NW >= 2, "tile shape");
     static_assert(TM == 1 || TM == 2 || TM == 4 || TM == 8, "row blocks per wavefront");
-    // stage: A tile, 256 bytes of A scales (one per lane), 256 bytes of B scales
-    constexpr int SA_OFF = BM * 128, SB_OFF = SA_OFF + 256;
+    // stage: A tile, A scales (64 rows per copy instruction), 256 bytes of B scales
+    constexpr int SA_OFF = BM * 128, SB_OFF = SA_OFF + stream_sa_bytes(BM);
     constexpr int STAGE = stream_stage_bytes(BM);
-    static_assert(BM <= 64 && STAGE == SB_OFF + 256, "stage layout");
+    constexpr int SA_COPIES = (BM + 63) / 64;         // wavefronts NW-1, NW-2 .. copy A scales
+    static_assert(STAGE == SB_OFF + 256 && SA_COPIES < NW, "stage layout");
     static_assert(NS >= 2 && NS * STAGE <= kLdsBytesPerCu, "LDS ring");
     constexpr int A_INS = BM / 8;                     // 1 KB (8 rows) per wavefront copy
     constexpr int A_PER = (A_INS + NW - 1) / NW;
@@ -649,19 +650,20 @@ __global__ void __launch_bounds__(64 * NW) fp8bs_stream_kernel(GemmParams p) {
         // same number of memory operations per chunk on every path (the compiler counts
         // them to place its waits for the B registers).  Lanes past the tile's rows or
         // scale blocks copy a clamped in-range value into an unused LDS word.
-        if (wave == NW - 1) {
-            const uint8_t* sa_c = (const uint8_t*)(p.sfa +
-                (LAYOUT == kMasked ? (int64_t)tl.g * kchunks * p.sfa_ld : (int64_t)0) +
-                (int64_t)c * p.sfa_ld);
-            const uint32_t off = (uint32_t)min(tl.m0 + lane, p.sfa_ld - 1) * 4u;
-            __builtin_amdgcn_global_load_lds((const GLOBAL_AS void*)(sa_c + off),
-                                             (LDS_AS void*)(st + SA_OFF), 4, 0, 0);
-        } else {
-            const uint8_t* sb_c = (const uint8_t*)(p.sfb + (int64_t)tl.g * nsb * kchunks + c);
-            const uint32_t off = (uint32_t)min(tl.n0 / 128 + lane, nsb - 1) * (uint32_t)kchunks * 4u;
-            __builtin_amdgcn_global_load_lds((const GLOBAL_AS void*)(sb_c + off),
-                                             (LDS_AS void*)(st + SB_OFF), 4, 0, 0);
-        }
+        // A scales (wavefronts NW-1, NW-2, ..) or B scales (the others), chosen without a
+        // branch: a data-dependent branch around a copy would hide the copy count from the
+        // compiler's wait placement.
+        const int part = NW - 1 - wave;                // A-scale rows 64*part .. 64*part+63
+        const bool is_sa = part < SA_COPIES;
+        const uint8_t* sa_c = (const uint8_t*)(p.sfa +
+            (LAYOUT == kMasked ? (int64_t)tl.g * kchunks * p.sfa_ld : (int64_t)0) +
+            (int64_t)c * p.sfa_ld);
+        const uint8_t* sb_c = (const uint8_t*)(p.sfb + (int64_t)tl.g * nsb * kchunks + c);
+        const uint32_t sa_off = (uint32_t)min(tl.m0 + 64 * part + lane, p.sfa_ld - 1) * 4u;
+        const uint32_t sb_off = (uint32_t)min(tl.n0 / 128 + lane, nsb - 1) * (uint32_t)kchunks * 4u;
+        const uint8_t* src = is_sa ? sa_c + sa_off : sb_c + sb_off;
+        uint8_t* dst = st + (is_sa ? SA_OFF + 256 * part : SB_OFF);
+        __builtin_amdgcn_global_load_lds((const GLOBAL_AS void*)src, (LDS_AS void*)dst, 4, 0, 0);
     };
 
     auto load_a = [&](const uint8_t* st, int i) {
@@ -706,21 +708,40 @@ __global__ void __launch_bounds__(64 * NW) fp8bs_stream_kernel(GemmParams p) {
                     sb[j] = sbl[min(tl.n0 + wave * WTN + 16 * j, p.n - 1) / 128 - blk0];
             }
         }
+        // products in the order (i, j); the result of product k is promoted after product
+        // k+LAG has issued, so only LAG+1 partials are live
+        constexpr int LAG = 2;
+        f32x4 ring[LAG + 1];
+        auto promote = [&](int k) {
+            const int i = k / TN, j = k % TN;
+            acc[i][j] += ring[k % (LAG + 1)] * (sa[i] * sb[UNIFORM_SB ? 0 : j]);
+        };
         i32x8 fa = load_a(st, 0);
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             i32x8 fn;
             if (i + 1 < TM) fn = load_a(st, i + 1);
-            const float s_i = sa[i];
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
+                const int k = i * TN + j;
                 __builtin_amdgcn_s_setprio(1);
-                const f32x4 part = mfma_e4m3(bf[j], fa);
+                ring[k % (LAG + 1)] = mfma_e4m3(bf[j], fa);
                 __builtin_amdgcn_s_setprio(0);
-                acc[i][j] += part * (s_i * sb[UNIFORM_SB ? 0 : j]);
+                if (k >= LAG) promote(k - LAG);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // the MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // the promotion it covers
             }
             if (i + 1 < TM) fa = fn;
         }
+#pragma unroll
+        for (int k = TM * TN - LAG; k < TM * TN; ++k)
+            if (k >= 0) promote(k);
+        // Pin the promoted accumulators here: otherwise the compiler defers the promotions
+        // of a whole unrolled group of chunks and holds all their partials live at once.
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) asm volatile("" : "+v"(acc[i][j]));
     };
 
     i32x8 breg[NS][TN];

@@ -39,8 +39,10 @@ struct InstanceShape {
 constexpr int stage_bytes(int block_m, int block_n) {
     return (block_m + block_n) * 128 + block_m * 4 + 256;
 }
-// kStreamB: one stage holds the A tile, 256 bytes of A scales and 256 of B scales.
-constexpr int stream_stage_bytes(int block_m) { return block_m * 128 + 512; }
+// kStreamB: one stage holds the A tile, its A scales (at least 256 bytes: one per lane of
+// a copy instruction) and 256 bytes of B scales.
+constexpr int stream_sa_bytes(int block_m) { return block_m * 4 > 256 ? block_m * 4 : 256; }
+constexpr int stream_stage_bytes(int block_m) { return block_m * 128 + stream_sa_bytes(block_m) + 256; }
 constexpr int instance_lds_bytes(int kind, int block_m, int block_n, int stages) {
     return stages * (kind == kStreamB ? stream_stage_bytes(block_m) : stage_bytes(block_m, block_n));
 }
