@@ -6,7 +6,7 @@ run once, back to back, on one stream (default: the dense prefill sweep,
 M = 4096 x six (N, K) shapes).  Inputs are synthetic, seeded, and resident in
 HBM before timing starts.  Prints one JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--family F] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--family F] [--graph] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -79,6 +79,10 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=1536,
                     help="rows of D per shape the oracle computes for the CPU baseline")
     ap.add_argument("--per-shape-out", default="", help="also write per-shape results here")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture the step (and each shape) in HIP graphs and time replays: "
+                         "for families of short kernels, where per-call host overhead would "
+                         "otherwise be timed")
     args = ap.parse_args()
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, args.family)
@@ -89,7 +93,7 @@ def main():
         ingest_traffic(args.ingest_traffic[0], args.ingest_traffic[1], args.traffic_probe)
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has "
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); there is "
               "no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
 
@@ -166,21 +170,65 @@ def main():
 
     # ---- timed region: K steps; events around every launch on the launch stream ----
     stream = torch.cuda.current_stream(dev)
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in problems] for _ in range(args.steps)]
     step_start = torch.cuda.Event(enable_timing=True)
     step_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    step_start.record(stream)
-    for s in range(args.steps):
-        for i, q in enumerate(problems):
-            ev[s][i][0].record(stream)
-            launch(q)
-            ev[s][i][1].record(stream)
-    step_end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
+    if args.graph:
+        # one graph per shape (one call each) and one for the whole step
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for q in problems:
+                launch(q)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        shape_graphs = []
+        for q in problems:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                launch(q)
+            shape_graphs.append(g)
+        step_graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(step_graph):
+            for q in problems:
+                launch(q)
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            step_graph.replay()
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        step_start.record(stream)
+        for _ in range(args.steps):
+            step_graph.replay()
+        step_end.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        # per-shape launch time: K back-to-back replays of that shape's graph
+        shape_ms = []
+        for g in shape_graphs:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(args.steps):
+                g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            shape_ms.append([e0.elapsed_time(e1) / args.steps] * args.steps)
+    else:
+        ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in problems] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        step_start.record(stream)
+        for s in range(args.steps):
+            for i, q in enumerate(problems):
+                ev[s][i][0].record(stream)
+                launch(q)
+                ev[s][i][1].record(stream)
+        step_end.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        shape_ms = [[ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]
+                    for i in range(len(problems))]
     total_ms = step_start.elapsed_time(step_end)
     ms_per_step = total_ms / args.steps
 
@@ -190,7 +238,7 @@ def main():
     per_shape = []
     for i, q in enumerate(problems):
         p = q["p"]
-        times = sorted(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps))
+        times = sorted(shape_ms[i])
         avg_ms = sum(times) / len(times)
         med_ms = times[len(times) // 2]
         tflops = p.flops() / (avg_ms * 1e-3) / 1e12
@@ -231,7 +279,8 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "fp8e4m3", "data": "synthetic",
         "config": {"workload": FAMILY_NAMES[args.family], "family": args.family,
                    "shapes": [q["desc"]["name"] for q in problems],
-                   "gflop_per_step": flops_step / 1e9},
+                   "gflop_per_step": flops_step / 1e9,
+                   "timing": "graph replay" if args.graph else "eager launches"},
         "roofline": roof, "cpu_baseline": cpu,
         "per_shape": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in s.items()}
                       for s in per_shape],

@@ -15,9 +15,10 @@ says were measured; the numbers themselves stand in for those workloads):
   in "deepseek开源周第三天：DeepGEMM深度分析", pxiaoer.blog): A gets one FP32 scale
   per (row, 128-column group), B one per 128x128 block (the last block of an
   N that is not a multiple of 128 covers only its existing rows).
-  ``scale = max(amax, 1e-4) / 448`` in FP32 (the 1e-4 floor is this build's
-  choice, so that an all-zero group still has a finite scale), then
-  ``q = e4m3(clamp(x / scale, -448, 448))`` using torch's round-to-nearest-even
+  ``scale = max(amax, 1e-4) / 448`` in FP32 (the 1e-4 floor is not on the pages;
+  it keeps the scale of an all-zero group finite), then
+  ``q = e4m3(clamp(x * (448 / max(amax, 1e-4)), -448, 448))`` (each step rounded to
+  FP32: the inverse once per group, the product per element) using torch's round-to-nearest-even
   cast to ``float8_e4m3fn`` (OCP e4m3).  The clamp is needed because torch maps
   values beyond the e4m3 range to NaN instead of saturating.
 * Contiguous MoE layout: ``counts ~ Multinomial(total, [1/G] * G)``; expert g's
@@ -114,9 +115,10 @@ def quantize_rows_1x128(x: np.ndarray):
     assert K % 128 == 0
     t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
     g = t.reshape(*t.shape[:-1], K // 128, 128)
-    amax = g.abs().amax(dim=-1)
-    s = amax.clamp_min(SCALE_FLOOR) / E4M3_MAX
-    q = (g / s.unsqueeze(-1)).clamp(-E4M3_MAX, E4M3_MAX).reshape(t.shape)
+    amax = g.abs().amax(dim=-1).clamp_min(SCALE_FLOOR)
+    s = amax / E4M3_MAX
+    inv = E4M3_MAX / amax
+    q = (g * inv.unsqueeze(-1)).clamp(-E4M3_MAX, E4M3_MAX).reshape(t.shape)
     return _to_e4m3_bytes(q), s.numpy().astype(np.float32)
 
 
@@ -129,9 +131,10 @@ def quantize_blocks_128x128(x: np.ndarray):
     pad = nb * 128 - N
     tp = torch.nn.functional.pad(t, (0, 0, 0, pad)) if pad else t   # zero rows never raise amax
     blocks = tp.reshape(G, nb, 128, K // 128, 128)
-    amax = blocks.abs().amax(dim=(2, 4))                             # [G][nb][kb]
-    s = amax.clamp_min(SCALE_FLOOR) / E4M3_MAX
-    q = (blocks / s[:, :, None, :, None]).clamp(-E4M3_MAX, E4M3_MAX)
+    amax = blocks.abs().amax(dim=(2, 4)).clamp_min(SCALE_FLOOR)      # [G][nb][kb]
+    s = amax / E4M3_MAX
+    inv = E4M3_MAX / amax
+    q = (blocks * inv[:, :, None, :, None]).clamp(-E4M3_MAX, E4M3_MAX)
     q = q.reshape(G, nb * 128, K)[:, :N, :]
     return _to_e4m3_bytes(q.contiguous()), s.numpy().astype(np.float32)
 

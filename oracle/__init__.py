@@ -14,6 +14,9 @@ All arrays are in the oracle's *logical* layouts:
   B   uint8  [G][N][K] or [N][K]  OCP e4m3 bytes, one row per output column
   SB  f32    [G][ceil(N/128)][K/128]
   D   uint16 [rows][N]            BF16 bit patterns
+
+The quantisers (``quant_1x128``, ``quant_128x128``) produce A/SA and B/SB in
+these layouts from FP32 inputs.
 """
 from __future__ import annotations
 
@@ -66,6 +69,12 @@ def _load():
     for f in ("dense", "contiguous", "masked", "points"):
         getattr(lib, "fp8bs_oracle_" + f).restype = ctypes.c_int
     lib.fp8bs_oracle_num_threads.restype = ctypes.c_int
+    lib.fp8bs_oracle_enc_e4m3.argtypes = [ctypes.c_float]
+    lib.fp8bs_oracle_enc_e4m3.restype = ctypes.c_uint8
+    lib.fp8bs_oracle_quant_1x128.argtypes = [P, P, P, I64, I64]
+    lib.fp8bs_oracle_quant_1x128.restype = ctypes.c_int
+    lib.fp8bs_oracle_quant_128x128.argtypes = [P, P, P, I64, I64, I64]
+    lib.fp8bs_oracle_quant_128x128.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -158,3 +167,28 @@ def points(A, SA, B, SB, a_row, group, col):
     _check(_load().fp8bs_oracle_points(_ptr(A), _ptr(SA), _ptr(B), _ptr(SB), N, K, n,
                                        _ptr(a_row), _ptr(group), _ptr(col), _ptr(acc), _ptr(d)))
     return acc, d
+
+
+def enc_e4m3(x: float) -> int:
+    """Nearest OCP e4m3 code (ties to even) of an FP32 value of magnitude <= 448."""
+    return int(_load().fp8bs_oracle_enc_e4m3(float(x)))
+
+
+def quant_1x128(X):
+    """X float32 [rows][K] -> (Q uint8 [rows][K], S float32 [rows][K/128])."""
+    X = _f32(X)
+    rows, K = X.shape
+    Q = np.zeros((rows, K), dtype=np.uint8)
+    S = np.zeros((rows, max(K // 128, 0)), dtype=np.float32)
+    _check(_load().fp8bs_oracle_quant_1x128(_ptr(X), _ptr(Q), _ptr(S), rows, K))
+    return Q, S
+
+
+def quant_128x128(X):
+    """X float32 [G][N][K] -> (Q uint8 [G][N][K], S float32 [G][ceil(N/128)][K/128])."""
+    X = _f32(X)
+    G, N, K = X.shape
+    Q = np.zeros((G, N, K), dtype=np.uint8)
+    S = np.zeros((G, (N + 127) // 128, max(K // 128, 0)), dtype=np.float32)
+    _check(_load().fp8bs_oracle_quant_128x128(_ptr(X), _ptr(Q), _ptr(S), G, N, K))
+    return Q, S

@@ -225,6 +225,109 @@ ORACLE_API int fp8bs_oracle_points(const uint8_t* A, const float* SA, const uint
     return 0;
 }
 
+/* ---- quantisation (the step that produces A, SA, B and SB) ------------------
+ *
+ * [pxiaoer] FP8-training list ("细粒度量化", "在线量化"): activations are scaled per
+ * 1x128 block and weights per 128x128 block, the factor computed online from the
+ * block, and the values converted to FP8; [hada] "Giao diện GEMM và ràng buộc
+ * layout": casting to FP8 is left to the caller.  The pages print no formula; the
+ * reading used here (plainest maximum-abs scaling onto the e4m3 range):
+ *
+ *   a     = max(max_{block} |x|, 1e-4)                (FP32; the floor keeps an
+ *                                                      all-zero block finite)
+ *   scale = a / 448                                   (FP32 division, stored)
+ *   inv   = 448 / a                                   (FP32 division, once per block)
+ *   q     = e4m3(clamp(x * inv, -448, 448))           (FP32 product, then the
+ *                                                      nearest e4m3 value, ties
+ *                                                      to the even code)
+ *
+ * Every step is one IEEE FP32 operation (compiled with -ffp-contract=off), so the
+ * GPU quantiser reproduces the codes and scales bit for bit. */
+
+/* Nearest OCP e4m3 code of a value of magnitude at most 448, ties to the even code
+ * (a code's last bit is its mantissa's last bit); the sign is kept (so -0 -> 0x80).
+ * A plain search over the 127 non-negative finite codes, whose values increase
+ * with the code.  NaN or magnitude above 448: the NaN code with x's sign. */
+ORACLE_API uint8_t fp8bs_oracle_enc_e4m3(float x) {
+    uint8_t sign = signbit(x) ? 0x80u : 0u;
+    double a = fabs((double)x);
+    int code, best = 0;
+    double best_d;
+    if (isnan(x) || a > 448.0) return (uint8_t)(sign | 0x7Fu);
+    best_d = a;                                  /* distance to code 0 (value 0) */
+    for (code = 1; code <= 126; ++code) {
+        double d = fabs(a - fp8bs_oracle_dec_e4m3((uint8_t)code));
+        if (d < best_d || (d == best_d && (code & 1) == 0)) {
+            best = code;
+            best_d = d;
+        }
+    }
+    return (uint8_t)(sign | best);
+}
+
+static float block_scale_inputs(float amax, float* inv) {
+    const float a = amax < 1e-4f ? 1e-4f : amax;
+    *inv = 448.0f / a;
+    return a / 448.0f;
+}
+
+static uint8_t quantise_one(float x, float inv) {
+    float v = x * inv;
+    if (v > 448.0f) v = 448.0f;
+    if (v < -448.0f) v = -448.0f;
+    return fp8bs_oracle_enc_e4m3(v);
+}
+
+/* Activations: X[rows][K] (FP32; BF16 inputs are widened exactly by the caller) ->
+ * Q[rows][K] e4m3 bytes and S[rows][K/128] (logical layout).  Returns 0, or -1 when
+ * K is not a positive multiple of 128. */
+ORACLE_API int fp8bs_oracle_quant_1x128(const float* X, uint8_t* Q, float* S, int64_t rows,
+                                        int64_t K) {
+    int64_t r;
+    if (K < 128 || K % 128 != 0 || rows < 0) return -1;
+    init_dec_table();
+#pragma omp parallel for schedule(static)
+    for (r = 0; r < rows; ++r) {
+        const int64_t groups = K / 128;
+        int64_t c, k;
+        for (c = 0; c < groups; ++c) {
+            const float* x = X + r * K + 128 * c;
+            float amax = 0.0f, inv;
+            for (k = 0; k < 128; ++k)
+                if (fabsf(x[k]) > amax) amax = fabsf(x[k]);
+            S[r * groups + c] = block_scale_inputs(amax, &inv);
+            for (k = 0; k < 128; ++k) Q[r * K + 128 * c + k] = quantise_one(x[k], inv);
+        }
+    }
+    return 0;
+}
+
+/* Weights: X[G][N][K] -> Q[G][N][K] and S[G][ceil(N/128)][K/128]; the last row block
+ * of an N that is not a multiple of 128 covers only its existing rows. */
+ORACLE_API int fp8bs_oracle_quant_128x128(const float* X, uint8_t* Q, float* S, int64_t G,
+                                          int64_t N, int64_t K) {
+    int64_t nb = (N + 127) / 128, kb = K / 128, blk;
+    if (K < 128 || K % 128 != 0 || N < 1 || G < 1) return -1;
+    init_dec_table();
+#pragma omp parallel for schedule(static)
+    for (blk = 0; blk < G * nb * kb; ++blk) {
+        int64_t g = blk / (nb * kb), i = (blk / kb) % nb, c = blk % kb, n, k;
+        int64_t n1 = 128 * i + 128 < N ? 128 * i + 128 : N;
+        float amax = 0.0f, inv, sc;
+        for (n = 128 * i; n < n1; ++n)
+            for (k = 128 * c; k < 128 * c + 128; ++k) {
+                float v = fabsf(X[(g * N + n) * K + k]);
+                if (v > amax) amax = v;
+            }
+        sc = block_scale_inputs(amax, &inv);
+        S[(g * nb + i) * kb + c] = sc;
+        for (n = 128 * i; n < n1; ++n)
+            for (k = 128 * c; k < 128 * c + 128; ++k)
+                Q[(g * N + n) * K + k] = quantise_one(X[(g * N + n) * K + k], inv);
+    }
+    return 0;
+}
+
 /* Threads an OpenMP parallel region of this library would use. */
 ORACLE_API int fp8bs_oracle_num_threads(void) {
 #ifdef _OPENMP

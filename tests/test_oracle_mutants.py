@@ -27,7 +27,16 @@ MUTANTS = {
                             "uint16_t sign = signbit(x) ? 0x8000u : 0u; x = (double)(float)x;"),
     "masked_off_by_one": ("if (r >= valid) continue;", "if (r > valid) continue;"),
     "padding_written": ("if (g < 0 || g >= G) continue;", "if (g >= G) continue; if (g < 0) g = 0;"),
+    # quantiser
+    "enc_ties_to_odd": ("(d == best_d && (code & 1) == 0)", "(d == best_d && (code & 1) == 1)"),
+    "enc_truncates": ("double d = fabs(a - fp8bs_oracle_dec_e4m3((uint8_t)code));",
+                      "double d = a - fp8bs_oracle_dec_e4m3((uint8_t)code); if (d < 0) continue;"),
+    "scale_from_inverse": ("return a / 448.0f;", "return 1.0f / *inv;"),
+    "no_scale_floor": ("const float a = amax < 1e-4f ? 1e-4f : amax;", "const float a = amax;"),
+    "weight_block_skips_last_row": ("int64_t n1 = 128 * i + 128 < N ? 128 * i + 128 : N;",
+                                    "int64_t n1 = 128 * i + 127 < N ? 128 * i + 127 : N;"),
 }
+PIN_FILES = ["test_oracle_pins.py", "test_oracle_quant_pins.py"]
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
@@ -41,7 +50,7 @@ def test_pins_catch_planted_mistake(name, tmp_path):
     subprocess.run(["gcc", "-std=c11", "-O2", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared",
                     "-o", str(so), str(mut_c), "-lm"], check=True)
     env = dict(os.environ, FP8BS_ORACLE_LIB=str(so))
-    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider"] +
+                       [os.path.join(ROOT, "tests", f) for f in PIN_FILES],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"pins did not catch mutant {name}:\n{r.stdout[-2000:]}"
