@@ -172,6 +172,46 @@ int fp8bs_grouped_masked_nt_ws(const void* a, const float* sfa, const void* b, c
 int64_t fp8bs_workspace_size(int layout, int64_t m, int n, int k, int num_groups,
                              int expected_m);
 
+/* Element types of quantiser inputs. */
+typedef enum {
+    FP8BS_DTYPE_F32 = 0,
+    FP8BS_DTYPE_BF16 = 1
+} fp8bs_dtype;
+
+/*
+ * Quantisers: produce the GEMM operands from FP32 or BF16 values, with the
+ * fine-grained online scaling of the FP8-training list in
+ * "deepseek开源周第三天：DeepGEMM深度分析" (pxiaoer.blog: one factor per 1x128
+ * activation block and per 128x128 weight block, computed from the block, values
+ * converted to FP8); the pages leave this cast to the caller ([hada] "Giao diện
+ * GEMM và ràng buộc layout").  Per block, each step one IEEE FP32 operation:
+ *
+ *     a = max(max_block |x|, 1e-4);  scale = a / 448;  inv = 448 / a;
+ *     q = e4m3(clamp(x * inv, -448, 448))   (nearest e4m3 value, ties to even;
+ *                                            a negative value rounding to zero
+ *                                            gives 0x80)
+ *
+ * NaN inputs never raise a block's maximum and quantise to the NaN code.
+ *
+ * fp8bs_quantize_1x128 -- activations, `groups` slots of `rows` rows:
+ *   x    f32 or bf16 [groups][rows][k] row-major (16-byte aligned)
+ *   q    e4m3 [groups][rows][k] (written; 16-byte aligned)
+ *   sfa  f32 [groups][k/128][fp8bs_get_sfa_ld(rows)] MN-major, the layout the GEMM
+ *        entry points read (groups = 1: dense / contiguous A; groups = G: masked A).
+ *        Entries for rows r < rows are written; the alignment padding is not.
+ * fp8bs_quantize_128x128 -- weights:
+ *   x    f32 or bf16 [groups][n][k];  q  e4m3 [groups][n][k]
+ *   sfb  f32 [groups][ceil(n/128)][k/128]; the last row block of an n that is not a
+ *        multiple of 128 covers only its existing rows.
+ * k must be a positive multiple of 128.  Asynchronous on `stream`, no allocation;
+ * returns FP8BS_ERR_SHAPE / _POINTER / _UNSUPPORTED (unknown x_dtype) before
+ * launching, FP8BS_ERR_HIP if the launch fails; rows == 0 is a no-op.
+ */
+int fp8bs_quantize_1x128(const void* x, int x_dtype, void* q, float* sfa, int groups, int rows,
+                         int k, hipStream_t stream);
+int fp8bs_quantize_128x128(const void* x, int x_dtype, void* q, float* sfb, int groups, int n,
+                           int k, hipStream_t stream);
+
 /* Row alignment of expert segments in the contiguous layout (128).  Analogue
  * of get_mk_alignment_for_contiguous_layout (hada page, section "Tiện ích và
  * biến môi trường"). */

@@ -27,6 +27,7 @@ __all__ = [
     "get_mk_alignment", "get_sfa_ld", "set_num_cus", "get_num_cus", "plan_query",
     "workspace_size", "describe_config", "count_tiles", "instances", "force_instance",
     "force_splits", "status_string", "sfa_mn_major", "library_path", "FP8BSError",
+    "fp8bs_quantize_1x128", "fp8bs_quantize_128x128", "quantize_1x128", "quantize_128x128",
     "LAYOUT_DENSE", "LAYOUT_CONTIGUOUS", "LAYOUT_MASKED",
 ]
 
@@ -85,6 +86,10 @@ def _load():
     lib.fp8bs_workspace_size.restype = I64
     lib.fp8bs_force_splits.argtypes = [I]
     lib.fp8bs_force_splits.restype = I
+    lib.fp8bs_quantize_1x128.argtypes = [P, I, P, P, I, I, I, P]
+    lib.fp8bs_quantize_1x128.restype = I
+    lib.fp8bs_quantize_128x128.argtypes = [P, I, P, P, I, I, I, P]
+    lib.fp8bs_quantize_128x128.restype = I
     lib.fp8bs_describe_config.argtypes = [I, I64, I, I, I, I, ctypes.c_char_p, ctypes.c_size_t]
     lib.fp8bs_count_tiles.argtypes = [I, I64, I, I, I, I]
     lib.fp8bs_count_tiles.restype = I64
@@ -370,3 +375,82 @@ def fp8bs_grouped_masked_nt_ws(a, sfa, b, sfb, d, masked_m, expected_m: int = 0,
 dense_nt = fp8bs_dense_nt_ws
 grouped_contiguous_nt = fp8bs_grouped_contiguous_nt_ws
 grouped_masked_nt = fp8bs_grouped_masked_nt_ws
+
+
+# ---- quantisers ------------------------------------------------------------
+
+DTYPE_F32, DTYPE_BF16 = 0, 1
+
+
+def _x_dtype(x):
+    torch = _torch()
+    if x.dtype == torch.float32:
+        return DTYPE_F32
+    if x.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    raise TypeError(f"quantiser input must be float32 or bfloat16, got {x.dtype}")
+
+
+def fp8bs_quantize_1x128(x, q, sfa, stream=None):
+    """Activations x f32/bf16 [rows][k] or [G][rows][k] -> q e4m3 (same shape) and sfa
+    f32 MN-major [(G,) k/128, ld(rows)] (the GEMM's A-scale layout)."""
+    torch = _torch()
+    if x.dim() not in (2, 3):
+        raise ValueError("x must be [rows][k] or [G][rows][k]")
+    G = 1 if x.dim() == 2 else x.shape[0]
+    rows, k = x.shape[-2], x.shape[-1]
+    xp = _dev_ptr(x, "x", (torch.float32, torch.bfloat16))
+    qp = _dev_ptr(q, "q", _fp8_dtypes())
+    sp = _dev_ptr(sfa, "sfa", (torch.float32,))
+    if tuple(q.shape) != tuple(x.shape):
+        raise ValueError("q must have x's shape")
+    if k % 128 == 0 and sfa.numel() != G * (k // 128) * get_sfa_ld(rows):
+        raise ValueError("sfa must hold [G][k/128][ld(rows)] floats")
+    with torch.cuda.device(x.device):
+        st = _load().fp8bs_quantize_1x128(xp, _x_dtype(x), qp, sp, G, rows, k,
+                                          _stream_handle(stream, x.device))
+    _check(st, "fp8bs_quantize_1x128")
+
+
+def fp8bs_quantize_128x128(x, q, sfb, stream=None):
+    """Weights x f32/bf16 [n][k] or [G][n][k] -> q e4m3 (same shape), sfb f32
+    [(G,) ceil(n/128), k/128]."""
+    torch = _torch()
+    if x.dim() not in (2, 3):
+        raise ValueError("x must be [n][k] or [G][n][k]")
+    G = 1 if x.dim() == 2 else x.shape[0]
+    n, k = x.shape[-2], x.shape[-1]
+    xp = _dev_ptr(x, "x", (torch.float32, torch.bfloat16))
+    qp = _dev_ptr(q, "q", _fp8_dtypes())
+    sp = _dev_ptr(sfb, "sfb", (torch.float32,))
+    if tuple(q.shape) != tuple(x.shape):
+        raise ValueError("q must have x's shape")
+    if k % 128 == 0 and sfb.numel() != G * ((n + 127) // 128) * (k // 128):
+        raise ValueError("sfb must hold [G][ceil(n/128)][k/128] floats")
+    with torch.cuda.device(x.device):
+        st = _load().fp8bs_quantize_128x128(xp, _x_dtype(x), qp, sp, G, n, k,
+                                            _stream_handle(stream, x.device))
+    _check(st, "fp8bs_quantize_128x128")
+
+
+def quantize_1x128(x, stream=None):
+    """Allocating form: returns (q uint8, sfa f32 MN-major)."""
+    torch = _torch()
+    G = 1 if x.dim() == 2 else x.shape[0]
+    rows, k = x.shape[-2], x.shape[-1]
+    q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    shape = (k // 128, get_sfa_ld(rows)) if x.dim() == 2 else (G, k // 128, get_sfa_ld(rows))
+    sfa = torch.zeros(shape, dtype=torch.float32, device=x.device)
+    fp8bs_quantize_1x128(x, q, sfa, stream)
+    return q, sfa
+
+
+def quantize_128x128(x, stream=None):
+    """Allocating form: returns (q uint8, sfb f32)."""
+    torch = _torch()
+    n, k = x.shape[-2], x.shape[-1]
+    q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    shape = ((n + 127) // 128, k // 128) if x.dim() == 2 else (x.shape[0], (n + 127) // 128, k // 128)
+    sfb = torch.empty(shape, dtype=torch.float32, device=x.device)
+    fp8bs_quantize_128x128(x, q, sfb, stream)
+    return q, sfb

@@ -22,7 +22,7 @@ LIB = os.path.join(LIBDIR, "libfp8bs.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 ARCH = os.environ.get("FP8BS_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["fp8bs_gemm.hip", "fp8bs_api.cpp", "fp8bs_planner.cpp"]
+SOURCES = ["fp8bs_gemm.hip", "fp8bs_quant.hip", "fp8bs_api.cpp", "fp8bs_planner.cpp"]
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
