@@ -163,6 +163,35 @@ int fp8bs_grouped_masked_nt_ws(const void* a, const float* sfa, const void* b, c
                                int expected_m, int n, int k, void* workspace,
                                size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Power-of-two scale variants (packed UE8M0).  The same operation with every scale a
+ * power of two, given as an 8-bit biased exponent e (value 2^(e-127); E8M0, no sign,
+ * no mantissa; e = 255 is not a number) packed four K groups per 32-bit word -- the
+ * packed UE8M0 format [hada] "Giao diện GEMM và ràng buộc layout" describes for SM100
+ * (four UE8M0 values in one int).  Byte j (least significant first) of word w holds
+ * K group 4w + j:
+ *   sfa  int32 [ceil(k/512)][fp8bs_get_sfa_ld(rows)] MN-major (masked: per slot,
+ *        [num_groups][ceil(k/512)][ld(max_m)]); row r, group c at byte c%4 of
+ *        sfa[(c/4)*ld + r]
+ *   sfb  int32 [num_groups][ceil(n/128)][ceil(k/512)]; block (i, c) at byte c%4 of
+ *        sfb[(g*ceil(n/128) + i)*ceil(k/512) + c/4]
+ * Everything else (operands, D, valid rows, workspace and its split-K use, errors) is
+ * as for the _ws calls.  gfx950's block-scaled matrix instructions apply the factors
+ * and accumulate across K groups themselves, so there is no FP32 promotion step; the
+ * result is within the same bound of the exact value.
+ */
+int fp8bs_dense_nt_ue8m0(const void* a, const int32_t* sfa, const void* b, const int32_t* sfb,
+                         void* d, int m, int n, int k, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+int fp8bs_grouped_contiguous_nt_ue8m0(const void* a, const int32_t* sfa, const void* b,
+                                      const int32_t* sfb, void* d, const int32_t* grouped_layout,
+                                      int m_total, int n, int k, int num_groups, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream);
+int fp8bs_grouped_masked_nt_ue8m0(const void* a, const int32_t* sfa, const void* b,
+                                  const int32_t* sfb, void* d, const int32_t* masked_m,
+                                  int num_groups, int max_m, int expected_m, int n, int k,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Workspace bytes the planner's preferred plan uses for a request on the current
  * device (CU cap respected; `m` as in fp8bs_plan_query).  0 means the best plan
  * splits nothing.  Passing at least this much to a _ws call lets it use that
@@ -261,6 +290,7 @@ typedef struct {
     int64_t workspace_bytes; /* workspace the plan uses (0 when splits == 1)  */
     int kind;           /* 0: A and B tiles staged in LDS, persistent grid;
                            1: B streamed into registers, one workgroup per unit */
+    int ue8m0;          /* 1: the instance is also compiled for packed UE8M0 scales */
 } fp8bs_plan;
 
 /*

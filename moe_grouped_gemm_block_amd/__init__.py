@@ -28,6 +28,8 @@ __all__ = [
     "workspace_size", "describe_config", "count_tiles", "instances", "force_instance",
     "force_splits", "status_string", "sfa_mn_major", "library_path", "FP8BSError",
     "fp8bs_quantize_1x128", "fp8bs_quantize_128x128", "quantize_1x128", "quantize_128x128",
+    "fp8bs_dense_nt_ue8m0", "fp8bs_grouped_contiguous_nt_ue8m0", "fp8bs_grouped_masked_nt_ue8m0",
+    "ue8m0_exponents", "pack_ue8m0", "sfa_ue8m0_mn_major", "sfb_ue8m0",
     "LAYOUT_DENSE", "LAYOUT_CONTIGUOUS", "LAYOUT_MASKED",
 ]
 
@@ -50,7 +52,7 @@ class _Plan(ctypes.Structure):
                 ("wg_per_cu", ctypes.c_int), ("stages", ctypes.c_int), ("tiles", ctypes.c_int64),
                 ("grid", ctypes.c_int64), ("raster", ctypes.c_int), ("instance", ctypes.c_int),
                 ("splits", ctypes.c_int), ("workspace_bytes", ctypes.c_int64),
-                ("kind", ctypes.c_int)]
+                ("kind", ctypes.c_int), ("ue8m0", ctypes.c_int)]
 
 
 def library_path() -> str:
@@ -86,6 +88,12 @@ def _load():
     lib.fp8bs_workspace_size.restype = I64
     lib.fp8bs_force_splits.argtypes = [I]
     lib.fp8bs_force_splits.restype = I
+    lib.fp8bs_dense_nt_ue8m0.argtypes = [P, P, P, P, P, I, I, I, P, S, P]
+    lib.fp8bs_grouped_contiguous_nt_ue8m0.argtypes = [P, P, P, P, P, P, I, I, I, I, P, S, P]
+    lib.fp8bs_grouped_masked_nt_ue8m0.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P, S, P]
+    for f in ("fp8bs_dense_nt_ue8m0", "fp8bs_grouped_contiguous_nt_ue8m0",
+              "fp8bs_grouped_masked_nt_ue8m0"):
+        getattr(lib, f).restype = I
     lib.fp8bs_quantize_1x128.argtypes = [P, I, P, P, I, I, I, P]
     lib.fp8bs_quantize_1x128.restype = I
     lib.fp8bs_quantize_128x128.argtypes = [P, I, P, P, I, I, I, P]
@@ -454,3 +462,126 @@ def quantize_128x128(x, stream=None):
     sfb = torch.empty(shape, dtype=torch.float32, device=x.device)
     fp8bs_quantize_128x128(x, q, sfb, stream)
     return q, sfb
+
+
+# ---- power-of-two (packed UE8M0) scales -------------------------------------
+
+def ue8m0_exponents(s):
+    """Powers of two (float32 tensor) -> their biased E8M0 exponents e (s = 2^(e-127)),
+    int32.  Raises if a value is not a power of two in [2^-127, 2^127]."""
+    torch = _torch()
+    m, e = torch.frexp(s.float())
+    if not bool(torch.all(m == 0.5)):
+        raise ValueError("UE8M0 scales must be powers of two")
+    out = (e - 1 + 127).to(torch.int32)
+    if bool(torch.any(out < 0)) or bool(torch.any(out > 254)):
+        raise ValueError("UE8M0 exponent out of range")
+    return out
+
+
+def pack_ue8m0(e):
+    """Exponents [..., groups] -> int32 [..., ceil(groups/4)], byte j of word w = group 4w+j."""
+    torch = _torch()
+    kb = e.shape[-1]
+    w = (kb + 3) // 4
+    pad = torch.zeros(*e.shape[:-1], 4 * w, dtype=torch.int64, device=e.device)
+    pad[..., :kb] = e.to(torch.int64) & 0xFF
+    pad = pad.reshape(*e.shape[:-1], w, 4)
+    v = pad[..., 0] | (pad[..., 1] << 8) | (pad[..., 2] << 16) | (pad[..., 3] << 24)
+    v = torch.where(v >= 2 ** 31, v - 2 ** 32, v)
+    return v.to(torch.int32)
+
+
+def sfa_ue8m0_mn_major(sa):
+    """Power-of-two A scales [..., rows, K/128] -> packed int32 MN-major
+    [..., ceil(K/512), ld(rows)] (padding zero)."""
+    torch = _torch()
+    rows = sa.shape[-2]
+    packed = pack_ue8m0(ue8m0_exponents(sa))                 # [..., rows, w]
+    ld = get_sfa_ld(rows)
+    out = torch.zeros(*packed.shape[:-2], packed.shape[-1], ld, dtype=torch.int32,
+                      device=sa.device)
+    out[..., :, :rows] = packed.transpose(-1, -2)
+    return out.contiguous()
+
+
+def sfb_ue8m0(sb):
+    """Power-of-two B scales [..., ceil(N/128), K/128] -> packed int32
+    [..., ceil(N/128), ceil(K/512)]."""
+    return pack_ue8m0(ue8m0_exponents(sb)).contiguous()
+
+
+def _ue8m0_checks(sfa, sfb, a_slots, b_groups, rows, n, k):
+    torch = _torch()
+    w = (k // 128 + 3) // 4 if k % 128 == 0 else -1
+    if w > 0 and (sfa.numel() != a_slots * w * get_sfa_ld(rows)
+                  or sfb.numel() != b_groups * ((n + 127) // 128) * w):
+        raise ValueError("packed UE8M0 scale tensor sizes do not match the shapes")
+    return (_dev_ptr(sfa, "sfa", (torch.int32,)), _dev_ptr(sfb, "sfb", (torch.int32,)))
+
+
+def _opt_workspace(ws):
+    torch = _torch()
+    if ws is None:
+        return ctypes.c_void_p(None), 0
+    return _dev_ptr(ws, "workspace", (torch.uint8,), 1), ws.numel()
+
+
+def fp8bs_dense_nt_ue8m0(a, sfa, b, sfb, d, workspace=None, stream=None):
+    """Dense GEMM with packed UE8M0 scales (sfa int32 MN-major [ceil(k/512)][ld(m)],
+    sfb int32 [ceil(n/128)][ceil(k/512)]); workspace (uint8) optional, enables split-K."""
+    torch = _torch()
+    m, k = a.shape
+    n = b.shape[0]
+    ap = _dev_ptr(a, "a", _fp8_dtypes(), 2)
+    bp = _dev_ptr(b, "b", _fp8_dtypes(), 2)
+    dp = _dev_ptr(d, "d", _bf16_dtypes(), 2)
+    if b.shape[1] != k or tuple(d.shape) != (m, n):
+        raise ValueError("shape mismatch between a, b and d")
+    sap, sbp = _ue8m0_checks(sfa, sfb, 1, 1, m, n, k)
+    wp, wb = _opt_workspace(workspace)
+    with torch.cuda.device(a.device):
+        st = _load().fp8bs_dense_nt_ue8m0(ap, sap, bp, sbp, dp, m, n, k, wp, wb,
+                                          _stream_handle(stream, a.device))
+    _check(st, "fp8bs_dense_nt_ue8m0")
+
+
+def fp8bs_grouped_contiguous_nt_ue8m0(a, sfa, b, sfb, d, grouped_layout, workspace=None,
+                                      stream=None):
+    """Contiguous MoE layout with packed UE8M0 scales (sfb [g][ceil(n/128)][ceil(k/512)])."""
+    torch = _torch()
+    m, k = a.shape
+    g, n = b.shape[0], b.shape[1]
+    ap = _dev_ptr(a, "a", _fp8_dtypes(), 2)
+    bp = _dev_ptr(b, "b", _fp8_dtypes(), 3)
+    dp = _dev_ptr(d, "d", _bf16_dtypes(), 2)
+    lp = _dev_ptr(grouped_layout, "grouped_layout", (torch.int32,), 1)
+    if b.shape[2] != k or tuple(d.shape) != (m, n) or grouped_layout.shape[0] != m:
+        raise ValueError("shape mismatch between a, b, d and grouped_layout")
+    sap, sbp = _ue8m0_checks(sfa, sfb, 1, g, m, n, k)
+    wp, wb = _opt_workspace(workspace)
+    with torch.cuda.device(a.device):
+        st = _load().fp8bs_grouped_contiguous_nt_ue8m0(ap, sap, bp, sbp, dp, lp, m, n, k, g, wp,
+                                                       wb, _stream_handle(stream, a.device))
+    _check(st, "fp8bs_grouped_contiguous_nt_ue8m0")
+
+
+def fp8bs_grouped_masked_nt_ue8m0(a, sfa, b, sfb, d, masked_m, expected_m: int = 0,
+                                  workspace=None, stream=None):
+    """Masked MoE layout with packed UE8M0 scales (sfa [g][ceil(k/512)][ld(max_m)])."""
+    torch = _torch()
+    g, max_m, k = a.shape
+    n = b.shape[1]
+    ap = _dev_ptr(a, "a", _fp8_dtypes(), 3)
+    bp = _dev_ptr(b, "b", _fp8_dtypes(), 3)
+    dp = _dev_ptr(d, "d", _bf16_dtypes(), 3)
+    mp = _dev_ptr(masked_m, "masked_m", (torch.int32,), 1)
+    if b.shape[0] != g or b.shape[2] != k or tuple(d.shape) != (g, max_m, n):
+        raise ValueError("shape mismatch between a, b, d and masked_m")
+    sap, sbp = _ue8m0_checks(sfa, sfb, g, g, max_m, n, k)
+    wp, wb = _opt_workspace(workspace)
+    with torch.cuda.device(a.device):
+        st = _load().fp8bs_grouped_masked_nt_ue8m0(ap, sap, bp, sbp, dp, mp, g, max_m,
+                                                   int(expected_m), n, k, wp, wb,
+                                                   _stream_handle(stream, a.device))
+    _check(st, "fp8bs_grouped_masked_nt_ue8m0")

@@ -61,23 +61,24 @@ void format_plan(const fp8bs::Plan& pl, int layout, int64_t m, int n, int k, int
 
 // Plan for a request on the current device, honouring the test pins.
 int make_plan(int layout, int64_t m, int n, int k, int num_groups, int expected_m,
-              int64_t ws_bytes, int* cus_out, fp8bs::Plan* pl) {
+              int64_t ws_bytes, int* cus_out, fp8bs::Plan* pl, int scale_mode = fp8bs::kScaleF32) {
     const int cus = current_num_cus();
     if (cus <= 0) return FP8BS_ERR_HIP;
     *cus_out = cus;
-    int st = fp8bs::plan_request(layout, m, n, k, num_groups, expected_m, cus, ws_bytes, pl);
+    int st = fp8bs::plan_request(layout, m, n, k, num_groups, expected_m, cus, ws_bytes, pl,
+                                 scale_mode);
     if (st != FP8BS_OK) return st;
     const int forced = g_forced_instance.load(std::memory_order_relaxed);
     const int splits = ws_bytes > 0 ? g_forced_splits.load(std::memory_order_relaxed) : 1;
     if (forced >= 0 || splits > 0)
         st = fp8bs::plan_instance(forced >= 0 ? forced : pl->instance, splits, layout, m, n, k,
-                                  num_groups, expected_m, cus, ws_bytes, pl);
+                                  num_groups, expected_m, cus, ws_bytes, pl, scale_mode);
     return st;
 }
 
 int run(int layout, const void* a, const float* sfa, const void* b, const float* sfb, void* d,
         const int32_t* group_data, int64_t m, int n, int k, int num_groups, int expected_m,
-        void* ws, size_t ws_bytes, hipStream_t stream) {
+        void* ws, size_t ws_bytes, hipStream_t stream, int scale_mode = fp8bs::kScaleF32) {
     int st = fp8bs::validate_sizes(layout, m, n, k, num_groups);
     if (st != FP8BS_OK) return st;
     if (!aligned16(a) || !aligned16(sfa) || !aligned16(b) || !aligned16(sfb) || !aligned16(d))
@@ -88,7 +89,7 @@ int run(int layout, const void* a, const float* sfa, const void* b, const float*
     const int64_t ws_cap = ws_bytes > (size_t)INT64_MAX ? INT64_MAX : (int64_t)ws_bytes;
     int cus = 0;
     fp8bs::Plan pl;
-    st = make_plan(layout, m, n, k, num_groups, expected_m, ws_cap, &cus, &pl);
+    st = make_plan(layout, m, n, k, num_groups, expected_m, ws_cap, &cus, &pl, scale_mode);
     if (st != FP8BS_OK) return st;
     if (print_configs()) {
         char line[512];
@@ -115,7 +116,7 @@ int run(int layout, const void* a, const float* sfa, const void* b, const float*
     p.splits = pl.splits;
     p.units = (int)(pl.tiles * pl.splits);
     p.ws = pl.splits > 1 ? (float*)ws : nullptr;
-    const int err = fp8bs::launch_instance(pl, layout, p, stream);
+    const int err = fp8bs::launch_instance(pl, layout, scale_mode, p, stream);
     return err == (int)hipSuccess ? FP8BS_OK : FP8BS_ERR_HIP;
 }
 
@@ -165,6 +166,31 @@ int fp8bs_grouped_masked_nt_ws(const void* a, const float* sfa, const void* b, c
     if (num_groups < 1) return FP8BS_ERR_SHAPE;
     return run(fp8bs::kMasked, a, sfa, b, sfb, d, masked_m, max_m, n, k, num_groups, expected_m,
                workspace, workspace_bytes, stream);
+}
+
+int fp8bs_dense_nt_ue8m0(const void* a, const int32_t* sfa, const void* b, const int32_t* sfb,
+                         void* d, int m, int n, int k, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+    return run(fp8bs::kDense, a, (const float*)sfa, b, (const float*)sfb, d, nullptr, m, n, k, 1, 0,
+               workspace, workspace_bytes, stream, fp8bs::kScaleUE8M0);
+}
+
+int fp8bs_grouped_contiguous_nt_ue8m0(const void* a, const int32_t* sfa, const void* b,
+                                      const int32_t* sfb, void* d, const int32_t* grouped_layout,
+                                      int m_total, int n, int k, int num_groups, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
+    return run(fp8bs::kContiguous, a, (const float*)sfa, b, (const float*)sfb, d, grouped_layout,
+               m_total, n, k, num_groups, 0, workspace, workspace_bytes, stream,
+               fp8bs::kScaleUE8M0);
+}
+
+int fp8bs_grouped_masked_nt_ue8m0(const void* a, const int32_t* sfa, const void* b,
+                                  const int32_t* sfb, void* d, const int32_t* masked_m,
+                                  int num_groups, int max_m, int expected_m, int n, int k,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (num_groups < 1) return FP8BS_ERR_SHAPE;
+    return run(fp8bs::kMasked, a, (const float*)sfa, b, (const float*)sfb, d, masked_m, max_m, n,
+               k, num_groups, expected_m, workspace, workspace_bytes, stream, fp8bs::kScaleUE8M0);
 }
 
 int64_t fp8bs_workspace_size(int layout, int64_t m, int n, int k, int num_groups,

@@ -215,8 +215,14 @@ __device__ __forceinline__ int partial_index(int wave, int i, int j, int lane) {
     return ((wave * TM + i) * TN + j) * 64 + lane;
 }
 
-template <int BM, int BN, int WM, int WN, int NS, int LAYOUT>
+template <int BM, int BN, int WM, int WN, int NS, int LAYOUT, int SCALE>
 __global__ void __launch_bounds__(64 * WM * WN) fp8bs_gemm_kernel(GemmParams p) {
+    // SCALE == kScaleF32: FP32 scales, per-chunk promotion on the VALU.
+    // SCALE == kScaleUE8M0: power-of-two scales, E8M0 exponents packed four K groups per
+    // 32-bit word; the matrix core applies them (v_mfma_scale_*: each operand row's
+    // 32-element K blocks multiplied by 2^(e-127)) and accumulates across chunks itself,
+    // so there is no promotion step.
+    constexpr bool E8 = SCALE == kScaleUE8M0;
     constexpr int NW = WM * WN;                      // wavefronts per workgroup
     constexpr int WTM = BM / WM, WTN = BN / WN;      // wavefront sub-tile
     constexpr int TM = WTM / 16, TN = WTN / 16;      // 16x16 blocks per wavefront
@@ -331,19 +337,22 @@ __global__ void __launch_bounds__(64 * WM * WN) fp8bs_gemm_kernel(GemmParams p) 
                 dma16(b_base + off, (LDS_AS void*)(st + B_OFF + ins * 1024));
             }
         }
+        // scale words: one per K group (FP32), or one per four K groups (packed E8M0)
+        const int sgrps = E8 ? (kchunks + 3) / 4 : kchunks;
+        const int sgrp = E8 ? c / 4 : c;
         if (wave == NW - 1) {
             // the chunk's block_m A scales (MN-major: contiguous)
             const uint8_t* sa_base = (const uint8_t*)(p.sfa +
-                (LAYOUT == kMasked ? (int64_t)tl.g * kchunks * p.sfa_ld : (int64_t)0) +
-                (int64_t)c * p.sfa_ld);
+                (LAYOUT == kMasked ? (int64_t)tl.g * sgrps * p.sfa_ld : (int64_t)0) +
+                (int64_t)sgrp * p.sfa_ld);
             int r4 = tl.m0 + 4 * lane;                // rows past the scale array are unused
             if (r4 >= p.sfa_ld) r4 = 0;
             if (4 * lane < BM) dma16(sa_base + (uint32_t)r4 * 4u, (LDS_AS void*)(st + SA_OFF));
         } else {
             // the B-scale values of the column blocks the tile touches (every other
             // wavefront writes the same bytes)
-            const uint8_t* sb_base = (const uint8_t*)(p.sfb + (int64_t)tl.g * nsb * kchunks + c);
-            const uint32_t sb_off = (uint32_t)min(tl.n0 / 128 + lane, nsb - 1) * (uint32_t)kchunks * 4u;
+            const uint8_t* sb_base = (const uint8_t*)(p.sfb + (int64_t)tl.g * nsb * sgrps + sgrp);
+            const uint32_t sb_off = (uint32_t)min(tl.n0 / 128 + lane, nsb - 1) * (uint32_t)sgrps * 4u;
             if (lane < SB_SPAN)
                 __builtin_amdgcn_global_load_lds((const GLOBAL_AS void*)(sb_base + sb_off),
                                                  (LDS_AS void*)(st + SB_OFF), 4, 0, 0);
@@ -448,13 +457,23 @@ __global__ void __launch_bounds__(64 * WM * WN) fp8bs_gemm_kernel(GemmParams p) 
 
         const uint8_t* st = smem + sq * STAGE;
         float sc[TM][UNIFORM_SB ? 1 : TN];
+        int sae[E8 ? TM : 1], sbe[E8 ? (UNIFORM_SB ? 1 : TN) : 1];   // E8M0 exponents
         {
             ScaleRegs sr;
             load_scales(st, cur.tl, sr);
+            if constexpr (E8) {
+                const int sh = 8 * (c & 3);             // this chunk's byte of the packed word
 #pragma unroll
-            for (int i = 0; i < TM; ++i)
+                for (int i = 0; i < TM; ++i) sae[i] = (__builtin_bit_cast(int, sr.sa[i]) >> sh) & 0xFF;
 #pragma unroll
-                for (int j = 0; j < (UNIFORM_SB ? 1 : TN); ++j) sc[i][j] = sr.sa[i] * sr.sb[j];
+                for (int j = 0; j < (UNIFORM_SB ? 1 : TN); ++j)
+                    sbe[j] = (__builtin_bit_cast(int, sr.sb[j]) >> sh) & 0xFF;
+            } else {
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < (UNIFORM_SB ? 1 : TN); ++j) sc[i][j] = sr.sa[i] * sr.sb[j];
+            }
         }
         auto promote = [&](int o, int q, const f32x4& part) {
             const int i = STREAM_A ? o : q, j = STREAM_A ? q : o;
@@ -467,12 +486,23 @@ __global__ void __launch_bounds__(64 * WM * WN) fp8bs_gemm_kernel(GemmParams p) 
         f32x4 ring[LAG + 1];
         auto step = [&](int o, int q, const i32x8& fr, const i32x8* res) {
             const int k = o * NI + q;
-            __builtin_amdgcn_s_setprio(1);             // favour the wave that feeds the MFMA pipe
-            ring[k % (LAG + 1)] = STREAM_A ? mfma_e4m3(res[q], fr) : mfma_e4m3(fr, res[q]);
-            __builtin_amdgcn_s_setprio(0);
-            if (k >= LAG) promote((k - LAG) / NI, (k - LAG) % NI, ring[(k - LAG) % (LAG + 1)]);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // the MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);       // the promotion it covers
+            if constexpr (E8) {
+                const int i = STREAM_A ? o : q, j = STREAM_A ? q : o;
+                __builtin_amdgcn_s_setprio(1);
+                // first operand B rows (scale: their 128x128 block), second A rows (row scale)
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    STREAM_A ? res[q] : fr, STREAM_A ? fr : res[q], acc[i][j], 0, 0,
+                    0, sbe[UNIFORM_SB ? 0 : j], 0, sae[i]);
+                __builtin_amdgcn_s_setprio(0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            } else {
+                __builtin_amdgcn_s_setprio(1);         // favour the wave that feeds the MFMA pipe
+                ring[k % (LAG + 1)] = STREAM_A ? mfma_e4m3(res[q], fr) : mfma_e4m3(fr, res[q]);
+                __builtin_amdgcn_s_setprio(0);
+                if (k >= LAG) promote((k - LAG) / NI, (k - LAG) % NI, ring[(k - LAG) % (LAG + 1)]);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // the MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // the promotion it covers
+            }
         };
 
         // ---- streamed blocks 0 .. NO-2 ----
@@ -504,9 +534,11 @@ __global__ void __launch_bounds__(64 * WM * WN) fp8bs_gemm_kernel(GemmParams p) 
                 __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             }
             nr.first = STREAM_A ? load_a(nst, 0) : load_b(nst, 0);
+            if constexpr (!E8) {
 #pragma unroll
-            for (int k = NO * NI - LAG; k < NO * NI; ++k)
-                if (k >= 0) promote(k / NI, k % NI, ring[k % (LAG + 1)]);
+                for (int k = NO * NI - LAG; k < NO * NI; ++k)
+                    if (k >= 0) promote(k / NI, k % NI, ring[k % (LAG + 1)]);
+            }
         }
 
         if (c + 1 == cur.c1) {
@@ -833,25 +865,36 @@ __global__ void __launch_bounds__(64 * WM * WN) fp8bs_splitk_reduce(GemmParams p
 typedef void (*KernelFn)(GemmParams);
 
 struct InstanceEntry {
-    KernelFn fn[3];
+    KernelFn fn[3];            // FP32 scales, per layout
+    KernelFn fn_e8[3];         // packed UE8M0 scales, per layout (null: not compiled)
     KernelFn reduce[3];
     int threads;
 };
 
-template <int KIND, int BM, int BN, int WM, int WN, int NS, int LAYOUT>
+template <int KIND, int BM, int BN, int WM, int WN, int NS, int LAYOUT, int SCALE>
 constexpr KernelFn gemm_fn() {
     if constexpr (KIND == kStreamB) {
         static_assert(WM == 1, "B-streaming instances have one wavefront along M");
-        return fp8bs_stream_kernel<BM, BN, WN, NS, LAYOUT>;
+        if constexpr (SCALE == kScaleF32) return fp8bs_stream_kernel<BM, BN, WN, NS, LAYOUT>;
+        else return nullptr;
     } else {
-        return fp8bs_gemm_kernel<BM, BN, WM, WN, NS, LAYOUT>;
+        return fp8bs_gemm_kernel<BM, BN, WM, WN, NS, LAYOUT, SCALE>;
     }
 }
 
-#define FP8BS_INSTANCE(KIND, BM, BN, WM, WN, NS, OCC, CNS, TNS, SCNS, STNS)    \
-    {{gemm_fn<KIND, BM, BN, WM, WN, NS, kDense>(),                            \
-      gemm_fn<KIND, BM, BN, WM, WN, NS, kContiguous>(),                       \
-      gemm_fn<KIND, BM, BN, WM, WN, NS, kMasked>()},                          \
+template <int KIND, int BM, int BN, int WM, int WN, int NS, int LAYOUT, int E8>
+constexpr KernelFn e8_fn() {
+    if constexpr (E8) return gemm_fn<KIND, BM, BN, WM, WN, NS, LAYOUT, kScaleUE8M0>();
+    else return nullptr;
+}
+
+#define FP8BS_INSTANCE(KIND, BM, BN, WM, WN, NS, OCC, CNS, TNS, SCNS, STNS, E8)            \
+    {{gemm_fn<KIND, BM, BN, WM, WN, NS, kDense, kScaleF32>(),                              \
+      gemm_fn<KIND, BM, BN, WM, WN, NS, kContiguous, kScaleF32>(),                         \
+      gemm_fn<KIND, BM, BN, WM, WN, NS, kMasked, kScaleF32>()},                            \
+     {e8_fn<KIND, BM, BN, WM, WN, NS, kDense, E8>(),                                       \
+      e8_fn<KIND, BM, BN, WM, WN, NS, kContiguous, E8>(),                                  \
+      e8_fn<KIND, BM, BN, WM, WN, NS, kMasked, E8>()},                                     \
      {fp8bs_splitk_reduce<BM, BN, WM, WN, kDense>,                            \
       fp8bs_splitk_reduce<BM, BN, WM, WN, kContiguous>,                       \
       fp8bs_splitk_reduce<BM, BN, WM, WN, kMasked>},                          \
@@ -863,13 +906,16 @@ const InstanceEntry kEntries[] = {
 
 }  // namespace
 
-int launch_instance(const Plan& plan, int layout, const GemmParams& p, hipStream_t stream) {
+int launch_instance(const Plan& plan, int layout, int scale_mode, const GemmParams& p,
+                    hipStream_t stream) {
     if (plan.instance < 0 || plan.instance >= (int)(sizeof(kEntries) / sizeof(kEntries[0])))
         return (int)hipErrorInvalidValue;
     const InstanceEntry& e = kEntries[plan.instance];
+    const KernelFn fn = scale_mode == kScaleUE8M0 ? e.fn_e8[layout] : e.fn[layout];
+    if (!fn) return (int)hipErrorInvalidValue;
     GemmParams args = p;
     void* argv[] = {&args};
-    hipError_t err = hipLaunchKernel((const void*)e.fn[layout], dim3((unsigned)plan.grid),
+    hipError_t err = hipLaunchKernel((const void*)fn, dim3((unsigned)plan.grid),
                                      dim3(e.threads), argv, 0, stream);
     if (err != hipSuccess || p.splits == 1) return (int)err;
     // one workgroup per tile (tiles without valid rows return at once)

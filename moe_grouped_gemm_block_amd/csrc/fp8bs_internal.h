@@ -18,6 +18,10 @@ enum Layout : int { kDense = 0, kContiguous = 1, kMasked = 2 };
 //            bandwidth bounds the GEMM.
 enum Kind : int { kStaged = 0, kStreamB = 1 };
 
+// Scale formats: FP32 factors (promotion on the VALU), or power-of-two factors given as
+// E8M0 exponents packed four K groups per 32-bit word (applied by the matrix core).
+enum ScaleMode : int { kScaleF32 = 0, kScaleUE8M0 = 1 };
+
 // Shape of one compiled kernel instance: an output tile of block_m x block_n
 // computed by waves_m x waves_n wavefronts (64 lanes each), each owning a
 // (block_m / waves_m) x (block_n / waves_n) sub-tile made of 16x16 MFMA tiles,
@@ -32,6 +36,7 @@ struct InstanceShape {
     int tile_ns;         // cost model: CU time per tile (prologue / epilogue)
     int stream_chunk_ns; // the same two when the operands stream from HBM (few rows)
     int stream_tile_ns;
+    int ue8m0;           // 1: also compiled for packed UE8M0 scales
 };
 
 // LDS bytes of one pipeline stage: the A tile, the B tile (128 K bytes per
@@ -91,12 +96,13 @@ int64_t split_workspace_bytes(const InstanceShape& shape, int64_t tiles, int spl
 // caller offers at least that much workspace) and launch shape.
 // Returns FP8BS_OK or an error status.  No device access.
 int plan_request(int layout, int64_t m, int n, int k, int num_groups, int expected_m,
-                 int num_cus, int64_t workspace_bytes, Plan* out);
+                 int num_cus, int64_t workspace_bytes, Plan* out, int scale_mode = kScaleF32);
 
 // Launch shape for a given instance and split count (used when either is pinned;
 // splits < 1 picks the best split count for the instance within the workspace).
 int plan_instance(int instance, int splits, int layout, int64_t m, int n, int k, int num_groups,
-                  int expected_m, int num_cus, int64_t workspace_bytes, Plan* out);
+                  int expected_m, int num_cus, int64_t workspace_bytes, Plan* out,
+                  int scale_mode = kScaleF32);
 
 // Copies a plan into the public struct.
 void export_plan(const Plan& p, fp8bs_plan* out);
@@ -104,7 +110,8 @@ void export_plan(const Plan& p, fp8bs_plan* out);
 // Validates sizes for an entry point (FP8BS_OK or FP8BS_ERR_SHAPE).
 int validate_sizes(int layout, int64_t m, int n, int k, int num_groups);
 
-// Launches instance `plan.instance` for `layout`; returns a hipError_t value.
-int launch_instance(const Plan& plan, int layout, const GemmParams& p, hipStream_t stream);
+// Launches instance `plan.instance` for `layout` and scale format; returns a hipError_t value.
+int launch_instance(const Plan& plan, int layout, int scale_mode, const GemmParams& p,
+                    hipStream_t stream);
 
 }  // namespace fp8bs

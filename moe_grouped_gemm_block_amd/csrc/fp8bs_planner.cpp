@@ -16,8 +16,8 @@
 
 namespace fp8bs {
 
-#define FP8BS_INSTANCE(KIND, BM, BN, WM, WN, NS, OCC, CNS, TNS, SCNS, STNS) \
-    {KIND, BM, BN, WM, WN, NS, OCC, instance_lds_bytes(KIND, BM, BN, NS), CNS, TNS, SCNS, STNS},
+#define FP8BS_INSTANCE(KIND, BM, BN, WM, WN, NS, OCC, CNS, TNS, SCNS, STNS, E8) \
+    {KIND, BM, BN, WM, WN, NS, OCC, instance_lds_bytes(KIND, BM, BN, NS), CNS, TNS, SCNS, STNS, E8},
 const InstanceShape kInstances[] = {
 #include "fp8bs_instances.inc"
 };
@@ -169,11 +169,13 @@ void fill_launch(int i, const Request& r, int splits, Plan* out) {
 }  // namespace
 
 int plan_instance(int instance, int splits, int layout, int64_t m, int n, int k, int num_groups,
-                  int expected_m, int num_cus, int64_t workspace_bytes, Plan* out) {
+                  int expected_m, int num_cus, int64_t workspace_bytes, Plan* out,
+                  int scale_mode) {
     if (instance < 0 || instance >= kNumInstances || num_cus < 1) return FP8BS_ERR_UNSUPPORTED;
     const Request r = make_request(layout, m, n, k, num_groups, expected_m, num_cus, workspace_bytes);
     const InstanceShape& s = kInstances[instance];
     if (!instance_fits(r, s)) return FP8BS_ERR_UNSUPPORTED;
+    if (scale_mode == kScaleUE8M0 && !s.ue8m0) return FP8BS_ERR_UNSUPPORTED;
     int best_s = -1;
     if (splits >= 1) {
         if (estimate(r, s, splits) < 0) return FP8BS_ERR_UNSUPPORTED;
@@ -194,7 +196,7 @@ int plan_instance(int instance, int splits, int layout, int64_t m, int n, int k,
 }
 
 int plan_request(int layout, int64_t m, int n, int k, int num_groups, int expected_m,
-                 int num_cus, int64_t workspace_bytes, Plan* out) {
+                 int num_cus, int64_t workspace_bytes, Plan* out, int scale_mode) {
     int st = validate_sizes(layout, m, n, k, layout == kDense ? 1 : num_groups);
     if (st != FP8BS_OK) return st;
     if (num_cus < 1) return FP8BS_ERR_UNSUPPORTED;
@@ -204,6 +206,7 @@ int plan_request(int layout, int64_t m, int n, int k, int num_groups, int expect
     for (int i = 0; i < kNumInstances; ++i) {
         const InstanceShape& s = kInstances[i];
         if (!instance_fits(r, s)) continue;
+        if (scale_mode == kScaleUE8M0 && !s.ue8m0) continue;
         for (int sp = 1; sp <= kMaxSplits; ++sp) {
             const double t = estimate(r, s, sp);
             if (t < 0) continue;
@@ -236,6 +239,7 @@ void export_plan(const Plan& p, fp8bs_plan* out) {
     out->splits = p.splits;
     out->workspace_bytes = p.workspace_bytes;
     out->kind = p.shape.kind;
+    out->ue8m0 = p.shape.ue8m0;
 }
 
 }  // namespace fp8bs

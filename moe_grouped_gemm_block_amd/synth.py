@@ -109,20 +109,33 @@ def _to_e4m3_bytes(q: torch.Tensor) -> np.ndarray:
     return q.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
 
 
-def quantize_rows_1x128(x: np.ndarray):
-    """x float32 [..., K] -> (uint8 e4m3 [..., K], float32 scales [..., K/128])."""
+def _pow2_scale(amax: torch.Tensor):
+    """Power-of-two scale (UE8M0): the smallest 2^e >= amax / 448, and its inverse."""
+    e = torch.ceil(torch.log2(amax.double() / E4M3_MAX))
+    # log2 of a float32 ratio near a power of two: nudge so that 2^e >= amax/448 holds exactly
+    e = torch.where(torch.exp2(e) * E4M3_MAX < amax.double(), e + 1, e)
+    e = torch.where(torch.exp2(e - 1) * E4M3_MAX >= amax.double(), e - 1, e)
+    return torch.exp2(e).float(), torch.exp2(-e).float()
+
+
+def quantize_rows_1x128(x: np.ndarray, pow2: bool = False):
+    """x float32 [..., K] -> (uint8 e4m3 [..., K], float32 scales [..., K/128]).
+    pow2: scales rounded up to powers of two (the UE8M0 variant); x * 2^-e is exact."""
     K = x.shape[-1]
     assert K % 128 == 0
     t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
     g = t.reshape(*t.shape[:-1], K // 128, 128)
     amax = g.abs().amax(dim=-1).clamp_min(SCALE_FLOOR)
-    s = amax / E4M3_MAX
-    inv = E4M3_MAX / amax
+    if pow2:
+        s, inv = _pow2_scale(amax)
+    else:
+        s = amax / E4M3_MAX
+        inv = E4M3_MAX / amax
     q = (g * inv.unsqueeze(-1)).clamp(-E4M3_MAX, E4M3_MAX).reshape(t.shape)
     return _to_e4m3_bytes(q), s.numpy().astype(np.float32)
 
 
-def quantize_blocks_128x128(x: np.ndarray):
+def quantize_blocks_128x128(x: np.ndarray, pow2: bool = False):
     """x float32 [G][N][K] -> (uint8 [G][N][K], float32 [G][ceil(N/128)][K/128])."""
     G, N, K = x.shape
     assert K % 128 == 0
@@ -132,8 +145,11 @@ def quantize_blocks_128x128(x: np.ndarray):
     tp = torch.nn.functional.pad(t, (0, 0, 0, pad)) if pad else t   # zero rows never raise amax
     blocks = tp.reshape(G, nb, 128, K // 128, 128)
     amax = blocks.abs().amax(dim=(2, 4)).clamp_min(SCALE_FLOOR)      # [G][nb][kb]
-    s = amax / E4M3_MAX
-    inv = E4M3_MAX / amax
+    if pow2:
+        s, inv = _pow2_scale(amax)
+    else:
+        s = amax / E4M3_MAX
+        inv = E4M3_MAX / amax
     q = (blocks * inv[:, :, None, :, None]).clamp(-E4M3_MAX, E4M3_MAX)
     q = q.reshape(G, nb * 128, K)[:, :N, :]
     return _to_e4m3_bytes(q.contiguous()), s.numpy().astype(np.float32)
@@ -143,22 +159,22 @@ def _normals(rng: np.random.Generator, shape) -> np.ndarray:
     return rng.standard_normal(size=shape, dtype=np.float32)
 
 
-def _weights(rng, G, N, K):
+def _weights(rng, G, N, K, pow2=False):
     Bf = _normals(rng, (G, N, K))
-    B, SB = quantize_blocks_128x128(Bf)
+    B, SB = quantize_blocks_128x128(Bf, pow2)
     return B, SB
 
 
 def make_dense(M: int, N: int, K: int, seed: int, outlier_frac: float = 0.0,
-               name: str = "") -> Problem:
+               name: str = "", pow2: bool = False) -> Problem:
     rng = _rng(seed)
     Af = _normals(rng, (M, K))
     if outlier_frac > 0.0 and M > 0:
         n_out = max(1, int(round(outlier_frac * M)))
         rows = rng.choice(M, size=n_out, replace=False)
         Af[rows] *= 100.0
-    A, SA = quantize_rows_1x128(Af)
-    B, SB = _weights(rng, 1, N, K)
+    A, SA = quantize_rows_1x128(Af, pow2)
+    B, SB = _weights(rng, 1, N, K, pow2)
     return Problem("dense", M, N, K, 1, A, SA, B, SB, seed=seed, name=name)
 
 
@@ -175,27 +191,27 @@ def contiguous_layout(counts, align: int = MK_ALIGNMENT) -> np.ndarray:
 
 
 def make_contiguous(G: int, N: int, K: int, seed: int, total_rows: int = 32768,
-                    counts=None, name: str = "") -> Problem:
+                    counts=None, name: str = "", pow2: bool = False) -> Problem:
     rng = _rng(seed)
     if counts is None:
         counts = rng.multinomial(total_rows, [1.0 / G] * G)
     layout = contiguous_layout(counts)
     M = int(layout.shape[0])
     Af = _normals(rng, (M, K))
-    A, SA = quantize_rows_1x128(Af)
-    B, SB = _weights(rng, G, N, K)
+    A, SA = quantize_rows_1x128(Af, pow2)
+    B, SB = _weights(rng, G, N, K, pow2)
     return Problem("contiguous", M, N, K, G, A, SA, B, SB, layout=layout, seed=seed, name=name)
 
 
 def make_masked(G: int, max_m: int, N: int, K: int, seed: int, expected_m: int = 0,
-                masked_m=None, name: str = "") -> Problem:
+                masked_m=None, name: str = "", pow2: bool = False) -> Problem:
     rng = _rng(seed)
     if masked_m is None:
         masked_m = rng.integers(1, max_m + 1, size=G)
     masked_m = np.asarray(masked_m, dtype=np.int32)
     Af = _normals(rng, (G, max_m, K))
-    A, SA = quantize_rows_1x128(Af)
-    B, SB = _weights(rng, G, N, K)
+    A, SA = quantize_rows_1x128(Af, pow2)
+    B, SB = _weights(rng, G, N, K, pow2)
     return Problem("masked", G * max_m, N, K, G, A, SA, B, SB, masked_m=masked_m, max_m=max_m,
                    expected_m=expected_m or max_m, seed=seed, name=name)
 
