@@ -69,6 +69,8 @@ def _load():
     for f in ("dense", "contiguous", "masked", "points"):
         getattr(lib, "fp8bs_oracle_" + f).restype = ctypes.c_int
     lib.fp8bs_oracle_num_threads.restype = ctypes.c_int
+    lib.fp8bs_oracle_with_addend.argtypes = [ctypes.c_int, P, P, P, P, P, P, P, I64, I64, I64, I64]
+    lib.fp8bs_oracle_with_addend.restype = ctypes.c_int
     lib.fp8bs_oracle_enc_e4m3.argtypes = [ctypes.c_float]
     lib.fp8bs_oracle_enc_e4m3.restype = ctypes.c_uint8
     lib.fp8bs_oracle_quant_1x128.argtypes = [P, P, P, I64, I64]
@@ -192,3 +194,20 @@ def quant_128x128(X):
     S = np.zeros((G, (N + 127) // 128, max(K // 128, 0)), dtype=np.float32)
     _check(_load().fp8bs_oracle_quant_128x128(_ptr(X), _ptr(Q), _ptr(S), G, N, K))
     return Q, S
+
+
+def with_addend(kind, A, SA, B, SB, C, D, gdata=None):
+    """D = bf16(C + A B^T) at valid rows, D updated in place.  kind: "dense" (A [M][K],
+    B [N][K] or [1][N][K]), "contiguous" (gdata = grouped_layout), "masked" (A [G][max_m][K],
+    gdata = masked_m).  C float32 with D's shape."""
+    A, SA, B, SB, C = _u8(A), _f32(SA), _u8(B), _f32(SB), _f32(C)
+    K = A.shape[-1]
+    N = B.shape[-2]
+    k = {"dense": 0, "contiguous": 1, "masked": 2}[kind]
+    G = 1 if B.ndim == 2 else B.shape[0]
+    rows = A.shape[1] if kind == "masked" else A.shape[0]
+    assert D.dtype == np.uint16 and D.flags["C_CONTIGUOUS"] and C.shape == D.shape
+    gd = _i32(gdata if gdata is not None else np.zeros(1, np.int32))
+    _check(_load().fp8bs_oracle_with_addend(k, _ptr(A), _ptr(SA), _ptr(B), _ptr(SB), _ptr(gd),
+                                            _ptr(C), _ptr(D), G, rows, N, K))
+    return D

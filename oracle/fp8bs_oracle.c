@@ -203,6 +203,38 @@ ORACLE_API int fp8bs_oracle_masked(const uint8_t* A, const float* SA, const uint
     return 0;
 }
 
+/* With an FP32 addend: D = bf16(C + A * B^T), the sum taken in FP64 before the single
+ * rounding ([hada] "Giao diện GEMM và ràng buộc layout": fp8_gemm_nt computes
+ * D = C + A @ B.T).  C has D's shape and layout ([rows][N], masked [G][max_m][N]); only
+ * valid rows of C are read.  layout / masked_m / G select the layout exactly as in the
+ * three functions above (kind 0 dense, 1 contiguous, 2 masked). */
+ORACLE_API int fp8bs_oracle_with_addend(int kind, const uint8_t* A, const float* SA,
+                                        const uint8_t* B, const float* SB, const int32_t* gdata,
+                                        const float* C, uint16_t* D, int64_t G, int64_t rows,
+                                        int64_t N, int64_t K) {
+    int64_t i;
+    if (!shape_ok(N, K) || rows < 0 || G <= 0 || kind < 0 || kind > 2) return -1;
+    init_dec_table();
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < (kind == 2 ? G * rows : rows); ++i) {
+        int64_t g = 0, n;
+        if (kind == 1) {
+            g = gdata[i];
+            if (g < 0 || g >= G) continue;
+        } else if (kind == 2) {
+            int64_t valid = gdata[i / rows];
+            if (valid < 0) valid = 0;
+            if (valid > rows) valid = rows;
+            g = i / rows;
+            if (i % rows >= valid) continue;
+        }
+        for (n = 0; n < N; ++n)
+            D[i * N + n] = fp8bs_oracle_bf16_rne((double)C[i * N + n] +
+                                                 dense_element(A, SA, B, SB, i, g, n, N, K));
+    }
+    return 0;
+}
+
 /* Sampled outputs, for shapes too large to compute whole.  Point p names an
  * A row a_row[p] (an index into the flattened A / SA rows), the group whose B
  * it meets, group[p], and a column col[p].  The caller maps layout-specific

@@ -33,6 +33,9 @@ MUTANTS = {
                       "double d = a - fp8bs_oracle_dec_e4m3((uint8_t)code); if (d < 0) continue;"),
     "scale_from_inverse": ("return a / 448.0f;", "return 1.0f / *inv;"),
     "no_scale_floor": ("const float a = amax < 1e-4f ? 1e-4f : amax;", "const float a = amax;"),
+    "addend_dropped": ("fp8bs_oracle_bf16_rne((double)C[i * N + n] +",
+                       "fp8bs_oracle_bf16_rne(0.0 * (double)C[i * N + n] +"),
+    "addend_masked_slot_rows": ("if (i % rows >= valid) continue;", "if (i % rows > valid) continue;"),
     "weight_block_skips_last_row": ("int64_t n1 = 128 * i + 128 < N ? 128 * i + 128 : N;",
                                     "int64_t n1 = 128 * i + 127 < N ? 128 * i + 127 : N;"),
 }

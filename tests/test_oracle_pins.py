@@ -361,3 +361,36 @@ def test_rejects_k_not_multiple_of_128():
     B = np.zeros((3, 200), np.uint8)
     with pytest.raises(ValueError):
         oracle.dense(A, np.ones((2, 1), np.float32), B, np.ones((1, 1), np.float32))
+
+
+def test_addend_reduces_to_the_plain_product_plus_c():
+    """D = C + A B^T: with C = 0 it is the plain product; with C = -(the FP64 product) it is
+    zero wherever that product is exactly representable as FP32; and in general it is the
+    FP64 sum of C and the exact product, rounded once (checked against the points entry)."""
+    from moe_grouped_gemm_block_amd import synth
+    p = synth.make_dense(40, 70, 384, seed=21)
+    D0 = oracle.dense(p.A, p.SA, p.B[0], p.SB[0])
+    Dz = np.zeros_like(D0)
+    oracle.with_addend("dense", p.A, p.SA, p.B[0], p.SB[0], np.zeros((40, 70), np.float32), Dz)
+    assert np.array_equal(Dz, D0)
+    rng = np.random.default_rng(22)
+    C = (rng.standard_normal((40, 70)) * 10).astype(np.float32)
+    Dc = np.zeros_like(D0)
+    oracle.with_addend("dense", p.A, p.SA, p.B[0], p.SB[0], C, Dc)
+    rows, cols = np.meshgrid(np.arange(40), np.arange(70), indexing="ij")
+    acc, _ = oracle.points(p.A, p.SA, p.B[0], p.SB[0], rows.ravel(), np.zeros(40 * 70, np.int64),
+                           cols.ravel())
+    want = np.array([oracle.bf16_rne(float(c) + float(a)) for c, a in zip(C.ravel(), acc)],
+                    dtype=np.uint16).reshape(40, 70)
+    assert np.array_equal(Dc, want)
+    # masked: invalid rows untouched, valid rows as dense per slot
+    q = synth.make_masked(2, 24, 70, 256, seed=23, masked_m=[5, 24])
+    Cm = rng.standard_normal((2, 24, 70)).astype(np.float32)
+    Dm = np.full((2, 24, 70), 0x7FC1, np.uint16)
+    oracle.with_addend("masked", q.A, q.SA, q.B, q.SB, Cm, Dm, q.masked_m)
+    assert np.all(Dm[0, 5:] == 0x7FC1)
+    for g in range(2):
+        ref = np.zeros((24, 70), np.uint16)
+        oracle.with_addend("dense", q.A[g], q.SA[g], q.B[g], q.SB[g], Cm[g], ref)
+        v = int(min(q.masked_m[g], 24))
+        assert np.array_equal(Dm[g, :v], ref[:v])
