@@ -32,7 +32,7 @@
  *       DG_PRINT_CONFIGS.
  *   - "deepseek开源周第三天：DeepGEMM深度分析", pxiaoer.blog: the FP8 training
  *     list (1x128 activation tiles, 128x128 weight blocks, FP32 accumulation).
- *   The "+ C" term of the pages' naming is not part of this operation.
+ *   The "+ C" term of the pages' naming is available through the _c entry points.
  *
  * Conventions shared by every entry point:
  *   - All tensor pointers are DEVICE pointers on the current HIP device; the
@@ -162,6 +162,28 @@ int fp8bs_grouped_masked_nt_ws(const void* a, const float* sfa, const void* b, c
                                void* d, const int32_t* masked_m, int num_groups, int max_m,
                                int expected_m, int n, int k, void* workspace,
                                size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Addend variants: D = bf16(C + A * B^T) -- the full NT form of [hada] "Giao diện GEMM
+ * và ràng buộc layout" (fp8_gemm_nt computes D = C + A @ B.T).  c is FP32 with D's
+ * shape and layout ([rows][n], masked [num_groups][max_m][n], row stride n, 16-byte
+ * aligned); it is read only at D's valid rows and columns, added to the FP32
+ * accumulator once, after the last K chunk (after the split-K reduction when K is
+ * split), and the sum is rounded once to BF16.  c may not overlap d.  Otherwise as
+ * the _ws calls.
+ */
+int fp8bs_dense_nt_c(const void* a, const float* sfa, const void* b, const float* sfb,
+                     const float* c, void* d, int m, int n, int k, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream);
+int fp8bs_grouped_contiguous_nt_c(const void* a, const float* sfa, const void* b,
+                                  const float* sfb, const float* c, void* d,
+                                  const int32_t* grouped_layout, int m_total, int n, int k,
+                                  int num_groups, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
+int fp8bs_grouped_masked_nt_c(const void* a, const float* sfa, const void* b, const float* sfb,
+                              const float* c, void* d, const int32_t* masked_m, int num_groups,
+                              int max_m, int expected_m, int n, int k, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Power-of-two scale variants (packed UE8M0).  The same operation with every scale a

@@ -30,6 +30,7 @@ __all__ = [
     "fp8bs_quantize_1x128", "fp8bs_quantize_128x128", "quantize_1x128", "quantize_128x128",
     "fp8bs_dense_nt_ue8m0", "fp8bs_grouped_contiguous_nt_ue8m0", "fp8bs_grouped_masked_nt_ue8m0",
     "ue8m0_exponents", "pack_ue8m0", "sfa_ue8m0_mn_major", "sfb_ue8m0",
+    "fp8bs_dense_nt_c", "fp8bs_grouped_contiguous_nt_c", "fp8bs_grouped_masked_nt_c",
     "LAYOUT_DENSE", "LAYOUT_CONTIGUOUS", "LAYOUT_MASKED",
 ]
 
@@ -88,6 +89,11 @@ def _load():
     lib.fp8bs_workspace_size.restype = I64
     lib.fp8bs_force_splits.argtypes = [I]
     lib.fp8bs_force_splits.restype = I
+    lib.fp8bs_dense_nt_c.argtypes = [P, P, P, P, P, P, I, I, I, P, S, P]
+    lib.fp8bs_grouped_contiguous_nt_c.argtypes = [P, P, P, P, P, P, P, I, I, I, I, P, S, P]
+    lib.fp8bs_grouped_masked_nt_c.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, P, S, P]
+    for f in ("fp8bs_dense_nt_c", "fp8bs_grouped_contiguous_nt_c", "fp8bs_grouped_masked_nt_c"):
+        getattr(lib, f).restype = I
     lib.fp8bs_dense_nt_ue8m0.argtypes = [P, P, P, P, P, I, I, I, P, S, P]
     lib.fp8bs_grouped_contiguous_nt_ue8m0.argtypes = [P, P, P, P, P, P, I, I, I, I, P, S, P]
     lib.fp8bs_grouped_masked_nt_ue8m0.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P, S, P]
@@ -585,3 +591,52 @@ def fp8bs_grouped_masked_nt_ue8m0(a, sfa, b, sfb, d, masked_m, expected_m: int =
                                                    int(expected_m), n, k, wp, wb,
                                                    _stream_handle(stream, a.device))
     _check(st, "fp8bs_grouped_masked_nt_ue8m0")
+
+
+# ---- D = C + A B^T ---------------------------------------------------------
+
+def _addend(c, d):
+    torch = _torch()
+    if tuple(c.shape) != tuple(d.shape):
+        raise ValueError("c must have d's shape")
+    return _dev_ptr(c, "c", (torch.float32,))
+
+
+def fp8bs_dense_nt_c(a, sfa, b, sfb, c, d, workspace=None, stream=None):
+    """D = bf16(C + A B^T): fp8bs_dense_nt_ws with an FP32 addend c [m][n]."""
+    args, m, n, k = _dense_args(a, sfa, b, sfb, d)
+    cp = _addend(c, d)
+    with _torch().cuda.device(a.device):
+        s = _stream(stream, a.device)
+        wp, wb, _keep = _workspace(workspace, LAYOUT_DENSE, m, n, k, 1, 0, s, a.device)
+        st = _load().fp8bs_dense_nt_c(*args[:4], cp, args[4], m, n, k, wp, wb,
+                                      ctypes.c_void_p(s.cuda_stream))
+    _check(st, "fp8bs_dense_nt_c")
+
+
+def fp8bs_grouped_contiguous_nt_c(a, sfa, b, sfb, c, d, grouped_layout, workspace=None,
+                                  stream=None):
+    """Contiguous MoE layout with an FP32 addend c [m_total][n]."""
+    args, m, n, k, g = _contiguous_args(a, sfa, b, sfb, d, grouped_layout)
+    cp = _addend(c, d)
+    with _torch().cuda.device(a.device):
+        s = _stream(stream, a.device)
+        wp, wb, _keep = _workspace(workspace, LAYOUT_CONTIGUOUS, m, n, k, g, 0, s, a.device)
+        st = _load().fp8bs_grouped_contiguous_nt_c(*args[:4], cp, args[4], args[5], m, n, k, g,
+                                                   wp, wb, ctypes.c_void_p(s.cuda_stream))
+    _check(st, "fp8bs_grouped_contiguous_nt_c")
+
+
+def fp8bs_grouped_masked_nt_c(a, sfa, b, sfb, c, d, masked_m, expected_m: int = 0,
+                              workspace=None, stream=None):
+    """Masked MoE layout with an FP32 addend c [g][max_m][n]."""
+    args, g, max_m, n, k = _masked_args(a, sfa, b, sfb, d, masked_m)
+    cp = _addend(c, d)
+    with _torch().cuda.device(a.device):
+        s = _stream(stream, a.device)
+        wp, wb, _keep = _workspace(workspace, LAYOUT_MASKED, max_m, n, k, g, int(expected_m), s,
+                                   a.device)
+        st = _load().fp8bs_grouped_masked_nt_c(*args[:4], cp, args[4], args[5], g, max_m,
+                                               int(expected_m), n, k, wp, wb,
+                                               ctypes.c_void_p(s.cuda_stream))
+    _check(st, "fp8bs_grouped_masked_nt_c")

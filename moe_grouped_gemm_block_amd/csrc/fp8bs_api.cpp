@@ -78,13 +78,15 @@ int make_plan(int layout, int64_t m, int n, int k, int num_groups, int expected_
 
 int run(int layout, const void* a, const float* sfa, const void* b, const float* sfb, void* d,
         const int32_t* group_data, int64_t m, int n, int k, int num_groups, int expected_m,
-        void* ws, size_t ws_bytes, hipStream_t stream, int scale_mode = fp8bs::kScaleF32) {
+        void* ws, size_t ws_bytes, hipStream_t stream, int scale_mode = fp8bs::kScaleF32,
+        const float* c = nullptr, bool want_c = false) {
     int st = fp8bs::validate_sizes(layout, m, n, k, num_groups);
     if (st != FP8BS_OK) return st;
     if (!aligned16(a) || !aligned16(sfa) || !aligned16(b) || !aligned16(sfb) || !aligned16(d))
         return FP8BS_ERR_POINTER;
     if (layout != fp8bs::kDense && !aligned4(group_data)) return FP8BS_ERR_POINTER;
     if (ws_bytes > 0 && !aligned16(ws)) return FP8BS_ERR_POINTER;
+    if (want_c && !aligned16(c)) return FP8BS_ERR_POINTER;
     if (m == 0) return FP8BS_OK;
     const int64_t ws_cap = ws_bytes > (size_t)INT64_MAX ? INT64_MAX : (int64_t)ws_bytes;
     int cus = 0;
@@ -116,6 +118,7 @@ int run(int layout, const void* a, const float* sfa, const void* b, const float*
     p.splits = pl.splits;
     p.units = (int)(pl.tiles * pl.splits);
     p.ws = pl.splits > 1 ? (float*)ws : nullptr;
+    p.c = want_c ? c : nullptr;
     const int err = fp8bs::launch_instance(pl, layout, scale_mode, p, stream);
     return err == (int)hipSuccess ? FP8BS_OK : FP8BS_ERR_HIP;
 }
@@ -166,6 +169,31 @@ int fp8bs_grouped_masked_nt_ws(const void* a, const float* sfa, const void* b, c
     if (num_groups < 1) return FP8BS_ERR_SHAPE;
     return run(fp8bs::kMasked, a, sfa, b, sfb, d, masked_m, max_m, n, k, num_groups, expected_m,
                workspace, workspace_bytes, stream);
+}
+
+int fp8bs_dense_nt_c(const void* a, const float* sfa, const void* b, const float* sfb,
+                     const float* c, void* d, int m, int n, int k, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+    return run(fp8bs::kDense, a, sfa, b, sfb, d, nullptr, m, n, k, 1, 0, workspace,
+               workspace_bytes, stream, fp8bs::kScaleF32, c, true);
+}
+
+int fp8bs_grouped_contiguous_nt_c(const void* a, const float* sfa, const void* b,
+                                  const float* sfb, const float* c, void* d,
+                                  const int32_t* grouped_layout, int m_total, int n, int k,
+                                  int num_groups, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
+    return run(fp8bs::kContiguous, a, sfa, b, sfb, d, grouped_layout, m_total, n, k, num_groups,
+               0, workspace, workspace_bytes, stream, fp8bs::kScaleF32, c, true);
+}
+
+int fp8bs_grouped_masked_nt_c(const void* a, const float* sfa, const void* b, const float* sfb,
+                              const float* c, void* d, const int32_t* masked_m, int num_groups,
+                              int max_m, int expected_m, int n, int k, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+    if (num_groups < 1) return FP8BS_ERR_SHAPE;
+    return run(fp8bs::kMasked, a, sfa, b, sfb, d, masked_m, max_m, n, k, num_groups, expected_m,
+               workspace, workspace_bytes, stream, fp8bs::kScaleF32, c, true);
 }
 
 int fp8bs_dense_nt_ue8m0(const void* a, const int32_t* sfa, const void* b, const int32_t* sfb,

@@ -181,7 +181,8 @@ __device__ __forceinline__ bool next_unit(const GemmParams& p, int u, Unit& w) {
 template <int TM, int TN, int WTM, int WTN, int LAYOUT>
 __device__ __forceinline__ void store_tile(const GemmParams& p, const Tile& tl, const f32x4 (&acc)[TM][TN],
                                            int wm, int wn, int lj, int kq, int flip) {
-    uint16_t* d_g = p.d + (LAYOUT == kMasked ? (int64_t)tl.g * p.m * p.n : (int64_t)0);
+    const int64_t slot = LAYOUT == kMasked ? (int64_t)tl.g * p.m * p.n : (int64_t)0;
+    uint16_t* d_g = p.d + slot;
     const bool vec_ok = (p.n & 3) == 0;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
@@ -190,10 +191,20 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const Tile& tl, 
         if (LAYOUT == kContiguous && ok) ok = p.grouped_layout[row] == tl.g;
         if (!ok) continue;
         uint16_t* drow = d_g + (int64_t)row * p.n;
+        const float* crow = p.c ? p.c + slot + (int64_t)row * p.n : nullptr;
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             const int col = tl.n0 + wn * WTN + 16 * j + 4 * kq;
-            const f32x4 v = acc[i][j];
+            f32x4 v = acc[i][j];
+            if (crow) {                                  // D = C + A B^T
+                if (vec_ok && col + 3 < p.n) {
+                    v += *(const f32x4*)(crow + col);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (col + e < p.n) v[e] += crow[col + e];
+                }
+            }
             if (vec_ok && col + 3 < p.n) {
                 uint2 w;
                 w.x = pack_bf16x2(v[0], v[1]);

@@ -77,6 +77,7 @@ struct GemmParams {
     int splits;         // K splits per tile (1: no workspace use)
     int units;          // tiles x splits
     float* ws;          // splits > 1: FP32 partial tiles, [tile][split][block_m*block_n]
+    const float* c;     // optional FP32 addend with D's shape (nullptr: none)
 };
 
 struct Plan {

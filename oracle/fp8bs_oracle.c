@@ -220,7 +220,7 @@ ORACLE_API int fp8bs_oracle_with_addend(int kind, const uint8_t* A, const float*
         int64_t g = 0, n;
         if (kind == 1) {
             g = gdata[i];
-            if (g < 0 || g >= G) continue;
+            if (!(g >= 0 && g < G)) continue;         /* padding row or unknown group */
         } else if (kind == 2) {
             int64_t valid = gdata[i / rows];
             if (valid < 0) valid = 0;
