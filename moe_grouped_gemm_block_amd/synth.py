@@ -27,6 +27,10 @@ says were measured; the numbers themselves stand in for those workloads):
   of "DeepGEMM: kernel FP8 GEMM sạch và hiệu quả nhờ scaling chi tiết",
   vi.news.hada.io: each expert segment aligned to the M block size).
 * Masked MoE layout: ``masked_m[g] ~ Uniform{1..max_m}``.
+* K-grouped (weight-gradient) layout: ``counts ~ Multinomial(total, [1/G] * G)``
+  tokens per expert, each group's K range rounded up to a multiple of 128 with
+  zero padding tokens; both operands are stored token-major ([K][M], [K][N]) and
+  quantised with one scale per feature and 128-token chunk.
 * Seeds: shape j of workload family i uses ``seed = 1000 * i + j``.
 """
 from __future__ import annotations
@@ -216,6 +220,85 @@ def make_masked(G: int, max_m: int, N: int, K: int, seed: int, expected_m: int =
                    expected_m=expected_m or max_m, seed=seed, name=name)
 
 
+def stored_operands(p: Problem, ab: str):
+    """A and B of a dense problem in the stored form ab ("nt", "nn", "tn", "tt"): A as
+    [M][K] ("n") or [K][M] ("t"), B as [N][K] ("t") or [K][N] ("n").  Same values; the
+    scales keep their layouts."""
+    assert p.kind == "dense" and ab in ("nt", "nn", "tn", "tt")
+    A = p.A if ab[0] == "n" else np.ascontiguousarray(p.A.T)
+    B = p.B[0] if ab[1] == "t" else np.ascontiguousarray(p.B[0].T)
+    return np.ascontiguousarray(A), np.ascontiguousarray(B)
+
+
+@dataclasses.dataclass
+class KGroupedProblem:
+    """K-grouped (weight-gradient) problem, host numpy arrays in logical layouts.
+
+    A:  uint8 [K_total][M]   (per token: the output gradient's M features)
+    B:  uint8 [K_total][N]   (per token: the layer input's N features)
+    SA: float32 [M][K_total/128], SB: float32 [N][K_total/128]
+        (one scale per feature and 128-token chunk)
+    ks: int64 [G] tokens per group along K, multiples of 128 (padding tokens are zero)
+    counts: int64 [G] real tokens per group (ks is counts rounded up to 128)
+    """
+    M: int
+    N: int
+    G: int
+    A: np.ndarray
+    SA: np.ndarray
+    B: np.ndarray
+    SB: np.ndarray
+    ks: np.ndarray
+    counts: np.ndarray
+    seed: int = 0
+    name: str = ""
+    kind: str = "k_grouped"
+
+    @property
+    def K(self) -> int:
+        return int(self.ks.sum())
+
+    def flops(self) -> float:
+        """2 * M * N * (real tokens): padding tokens are not counted."""
+        return 2.0 * self.M * self.N * float(self.counts.sum())
+
+    def algorithmic_bytes(self, with_c: bool = False) -> float:
+        """A + B + SA + SB once, D (FP32, every group) once, plus C when it is read."""
+        K = self.K
+        d = self.G * self.M * self.N * 4
+        return float(K * (self.M + self.N) + (K // 128) * (self.M + self.N) * 4 + d
+                     + (d if with_c else 0))
+
+
+def _quantize_along_k(x: np.ndarray, pow2: bool = False):
+    """x float32 [K][F] (K outermost) -> (uint8 [K][F], float32 [F][K/128]): one scale
+    per feature and 128-row chunk, the 1x128 recipe applied along K."""
+    q, s = quantize_rows_1x128(np.ascontiguousarray(x.T), pow2)
+    return np.ascontiguousarray(q.T), s
+
+
+def make_k_grouped(G: int, M: int, N: int, seed: int, total_tokens: int = 32768, counts=None,
+                   name: str = "", pow2: bool = False) -> KGroupedProblem:
+    rng = _rng(seed)
+    if counts is None:
+        counts = rng.multinomial(total_tokens, [1.0 / G] * G)
+    counts = np.asarray(counts, dtype=np.int64)
+    ks = (counts + MK_ALIGNMENT - 1) // MK_ALIGNMENT * MK_ALIGNMENT
+    K = int(ks.sum())
+    real = np.zeros(K, dtype=bool)                 # token rows that are not padding
+    k0 = 0
+    for c, k in zip(counts, ks):
+        real[k0:k0 + c] = True
+        k0 += int(k)
+    Xa = _normals(rng, (K, M))
+    Xb = _normals(rng, (K, N))
+    Xa[~real] = 0.0
+    Xb[~real] = 0.0
+    A, SA = _quantize_along_k(Xa, pow2)
+    B, SB = _quantize_along_k(Xb, pow2)
+    return KGroupedProblem(M, N, G, A, SA, B, SB, ks, counts, seed=seed, name=name)
+
+
 # ---- the workload families -------------------------------------------------
 
 DENSE_PREFILL_NK = [(2112, 7168), (24576, 1536), (32768, 512), (7168, 16384), (4096, 7168),
@@ -223,6 +306,8 @@ DENSE_PREFILL_NK = [(2112, 7168), (24576, 1536), (32768, 512), (7168, 16384), (4
 DECODE_M = [64, 128, 256]
 DECODE_NK = [(7168, 7168), (7168, 2048), (4096, 7168)]
 MOE_NK = [(4096, 7168), (7168, 2048)]
+# weight gradients of the two MoE projections above: dW [N_fwd][K_fwd] = dY^T X
+KGROUPED_MN = [(4096, 7168), (7168, 2048)]
 
 
 def workload_shapes(family: int) -> List[dict]:
@@ -249,6 +334,10 @@ def workload_shapes(family: int) -> List[dict]:
         for j, (n, k) in enumerate(MOE_NK):
             out.append(dict(kind="masked", G=16, max_m=256, N=n, K=k, expected_m=128,
                             seed=4000 + j, name=f"masked_g16_m256_n{n}_k{k}"))
+    elif family == 5:
+        for j, (m, n) in enumerate(KGROUPED_MN):
+            out.append(dict(kind="k_grouped", G=8, M=m, N=n, seed=5000 + j,
+                            name=f"kgrouped_g8_m{m}_n{n}"))
     else:
         raise ValueError(family)
     return out
@@ -266,4 +355,7 @@ def make(desc: dict) -> Problem:
     if kind == "masked":
         return make_masked(d["G"], d["max_m"], d["N"], d["K"], d["seed"], d.get("expected_m", 0),
                            masked_m=d.get("masked_m"), name=d.get("name", ""))
+    if kind == "k_grouped":
+        return make_k_grouped(d["G"], d["M"], d["N"], d["seed"], d.get("total_tokens", 32768),
+                              counts=d.get("counts"), name=d.get("name", ""))
     raise ValueError(kind)

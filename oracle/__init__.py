@@ -16,7 +16,10 @@ All arrays are in the oracle's *logical* layouts:
   D   uint16 [rows][N]            BF16 bit patterns
 
 The quantisers (``quant_1x128``, ``quant_128x128``) produce A/SA and B/SB in
-these layouts from FP32 inputs.
+these layouts from FP32 inputs.  ``dense_layout`` takes A and B in any of the four
+stored forms nt / nn / tn / tt; ``k_grouped`` is the K-grouped (weight-gradient)
+product with A [K_total][M], B [K_total][N], SA [M][K_total/128], SB [N][K_total/128]
+and FP32 output D [G][M][N].
 """
 from __future__ import annotations
 
@@ -77,6 +80,11 @@ def _load():
     lib.fp8bs_oracle_quant_1x128.restype = ctypes.c_int
     lib.fp8bs_oracle_quant_128x128.argtypes = [P, P, P, I64, I64, I64]
     lib.fp8bs_oracle_quant_128x128.restype = ctypes.c_int
+    lib.fp8bs_oracle_dense_layout.argtypes = [ctypes.c_int, ctypes.c_int, P, P, P, P, P, P,
+                                              I64, I64, I64]
+    lib.fp8bs_oracle_dense_layout.restype = ctypes.c_int
+    lib.fp8bs_oracle_k_grouped.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64]
+    lib.fp8bs_oracle_k_grouped.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -210,4 +218,49 @@ def with_addend(kind, A, SA, B, SB, C, D, gdata=None):
     gd = _i32(gdata if gdata is not None else np.zeros(1, np.int32))
     _check(_load().fp8bs_oracle_with_addend(k, _ptr(A), _ptr(SA), _ptr(B), _ptr(SB), _ptr(gd),
                                             _ptr(C), _ptr(D), G, rows, N, K))
+    return D
+
+
+def dense_layout(ab, A, SA, B, SB, C=None):
+    """D (BF16 bits, [M][N]) for the stored forms ab in {"nt", "nn", "tn", "tt"}:
+    A is [M][K] ("n" first) or [K][M] ("t"), B is [N][K] ("t" second) or [K][N] ("n").
+    SA [M][K/128] and SB [ceil(N/128)][K/128] as in ``dense``; C float32 [M][N] or None."""
+    assert ab in ("nt", "nn", "tn", "tt")
+    A, SA, B, SB = _u8(A), _f32(SA), _u8(B), _f32(SB)
+    a_t, b_t = ab[0] == "t", ab[1] == "t"
+    M, K = (A.shape[1], A.shape[0]) if a_t else A.shape
+    N = B.shape[0] if b_t else B.shape[1]
+    assert (B.shape[1] if b_t else B.shape[0]) == K, "A and B disagree on K"
+    D = np.zeros((M, N), dtype=np.uint16)
+    Cp = None
+    if C is not None:
+        C = _f32(C)
+        assert C.shape == (M, N)
+        Cp = _ptr(C)
+    _check(_load().fp8bs_oracle_dense_layout(int(a_t), int(b_t), _ptr(A), _ptr(SA), _ptr(B),
+                                             _ptr(SB), Cp, _ptr(D), M, N, K))
+    return D
+
+
+def k_grouped(A, SA, B, SB, ks, C=None):
+    """K-grouped product: A uint8 [K_total][M], B uint8 [K_total][N], SA float32
+    [M][K_total/128], SB float32 [N][K_total/128], ks the G group sizes along K (each a
+    multiple of 128, summing to K_total), C float32 [G][M][N] or None.  Returns FP32 D
+    [G][M][N]."""
+    A, SA, B, SB = _u8(A), _f32(SA), _u8(B), _f32(SB)
+    ks = np.ascontiguousarray(ks, dtype=np.int64)
+    K_total, M = A.shape
+    N = B.shape[1]
+    assert B.shape[0] == K_total
+    G = ks.shape[0]
+    D = np.zeros((G, M, N), dtype=np.float32)
+    Cp = None
+    if C is not None:
+        C = _f32(C)
+        assert C.shape == (G, M, N)
+        Cp = _ptr(C)
+    rc = _load().fp8bs_oracle_k_grouped(_ptr(A), _ptr(SA), _ptr(B), _ptr(SB), _ptr(ks), Cp,
+                                        _ptr(D), G, M, N, K_total)
+    if rc != 0:
+        raise ValueError("oracle rejected the group sizes (multiples of 128 summing to K_total)")
     return D

@@ -27,7 +27,9 @@
  *   "DeepGEMM" section: fine-grained scaling).
  * - The NT form D = A * B^T, A row-major [M][K], B stored [N][K] ([hada]
  *   "Giao diện GEMM và ràng buộc layout": fp8_gemm_nt computes D = C + A @ B.T,
- *   row-major x col-major).  This oracle has no C term.
+ *   row-major x col-major).  The C term is taken by fp8bs_oracle_with_addend and
+ *   the two functions further down; the other stored forms (nn, tn, tt) and the
+ *   K-grouped weight-gradient product are defined next to their functions.
  * - Each 128-K chunk's partial product is scaled and promoted into a wider
  *   accumulator ([README-zh] "DeepGEMM" section, two-level accumulation;
  *   [pxiaoer] "提高累加精度").  Here the wider accumulator is FP64.
@@ -116,18 +118,20 @@ static void init_dec_table(void) {
 }
 
 /* One output element before the final rounding.
- *   a:  K bytes of one A row;      sa: its K/128 scales, sa[c * sa_step]
- *   b:  K bytes of one B row (= one output column n);
- *   sb: the K/128 scales of B's 128-row block holding that column, sb[c * sb_step]
+ *   a:  the K bytes of one row of the product's left operand, a[k * a_step];
+ *   sa: its K/128 scales, sa[c * sa_step];
+ *   b:  the K bytes of the right operand for one output column n, b[k * b_step];
+ *   sb: the K/128 scales that apply to that column, sb[c * sb_step].
  * Chunks are visited in increasing order c = 0, 1, ... */
-static double element_acc(const uint8_t* a, const float* sa, ptrdiff_t sa_step,
-                          const uint8_t* b, const float* sb, ptrdiff_t sb_step,
+static double element_acc(const uint8_t* a, ptrdiff_t a_step, const float* sa, ptrdiff_t sa_step,
+                          const uint8_t* b, ptrdiff_t b_step, const float* sb, ptrdiff_t sb_step,
                           int64_t K) {
     double acc = 0.0;
     int64_t c, k;
     for (c = 0; c < K / 128; ++c) {
         double p = 0.0, s;
-        for (k = 128 * c; k < 128 * c + 128; ++k) p += dec_table[a[k]] * dec_table[b[k]];
+        for (k = 128 * c; k < 128 * c + 128; ++k)
+            p += dec_table[a[k * a_step]] * dec_table[b[k * b_step]];
         s = (double)sa[c * sa_step] * (double)sb[c * sb_step];
         acc += p * s;
     }
@@ -139,8 +143,8 @@ static double dense_element(const uint8_t* A, const float* SA, const uint8_t* B,
                             const float* SB, int64_t r, int64_t g, int64_t n,
                             int64_t N, int64_t K) {
     int64_t kb = K / 128, nb = (N + 127) / 128;
-    return element_acc(A + r * K, SA + r * kb, 1,
-                       B + (g * N + n) * K, SB + (g * nb + n / 128) * kb, 1, K);
+    return element_acc(A + r * K, 1, SA + r * kb, 1,
+                       B + (g * N + n) * K, 1, SB + (g * nb + n / 128) * kb, 1, K);
 }
 
 static int shape_ok(int64_t N, int64_t K) { return N > 0 && K >= 128 && K % 128 == 0; }
@@ -253,6 +257,94 @@ ORACLE_API int fp8bs_oracle_points(const uint8_t* A, const float* SA, const uint
         double v = dense_element(A, SA, B, SB, a_row[p], group[p], col[p], N, K);
         if (acc) acc[p] = v;
         d[p] = fp8bs_oracle_bf16_rne(v);
+    }
+    return 0;
+}
+
+/* ---- operand storage layouts: nt, nn, tn, tt ------------------------------
+ *
+ * [hada] "Giao diện GEMM và ràng buộc layout": the kernels are named for
+ * D = C + A @ B with two letters saying whether A and B enter as stored ("n") or
+ * transposed ("t") -- fp8_gemm_nt is D = C + A @ B.T -- and the newer kernels
+ * accept all four of nt, tn, nn, tt ([hada] "Dense và Grouped GEMM":
+ * fp8_gemm_{nt, nn, tn, tt}).  With every tensor stored row-major that reads:
+ *
+ *   nt: A [M][K], B [N][K]        nn: A [M][K], B [K][N]
+ *   tn: A [K][M], B [K][N]        tt: A [K][M], B [N][K]
+ *
+ * Only where the bytes sit changes.  The scales keep their logical layouts
+ * (SA [M][K/128], SB [ceil(N/128)][K/128]) and every output is the value defined
+ * at the top of this file (plus C when C is given). */
+ORACLE_API int fp8bs_oracle_dense_layout(int a_transposed, int b_transposed, const uint8_t* A,
+                                         const float* SA, const uint8_t* B, const float* SB,
+                                         const float* C, uint16_t* D, int64_t M, int64_t N,
+                                         int64_t K) {
+    int64_t r;
+    if (!shape_ok(N, K) || M < 0) return -1;
+    init_dec_table();
+#pragma omp parallel for schedule(static)
+    for (r = 0; r < M; ++r) {
+        const int64_t kb = K / 128;
+        /* row r of the left factor: stored as row r of A ("n") or column r ("t") */
+        const uint8_t* a = a_transposed ? A + r : A + r * K;
+        const ptrdiff_t a_step = a_transposed ? M : 1;
+        int64_t n;
+        for (n = 0; n < N; ++n) {
+            /* column n of the right factor: row n of B ("t") or column n ("n") */
+            const uint8_t* b = b_transposed ? B + n * K : B + n;
+            const ptrdiff_t b_step = b_transposed ? 1 : N;
+            double v = element_acc(a, a_step, SA + r * kb, 1, b, b_step, SB + (n / 128) * kb, 1, K);
+            if (C) v += (double)C[r * N + n];
+            D[r * N + n] = fp8bs_oracle_bf16_rne(v);
+        }
+    }
+    return 0;
+}
+
+/* ---- K-grouped product for MoE weight gradients ---------------------------
+ *
+ * [hada] "Dense và Grouped GEMM": besides grouping along M, there is a grouping
+ * along K for the MoE weight backward pass, with M and N fixed
+ * (k_grouped_fp8_gemm_tn_contiguous).  The reading used here (the pages print
+ * no formula):
+ *
+ * - tn form: A [K_total][M] and B [K_total][N], both stored with K outermost (the
+ *   output gradient and the layer input, one row per token); group g owns the
+ *   K rows [k_g, k_g + ks[g]), k_g = ks[0] + ... + ks[g-1], each ks[g] a multiple
+ *   of 128 (zero allowed), so no 128-row chunk straddles two groups;
+ * - both operands carry one FP32 scale per (row of the product, 128-K chunk), the
+ *   1x128 activation granularity of [pxiaoer] "细粒度量化" taken along K:
+ *   SA [M][K_total/128], SB [N][K_total/128] (logical layouts);
+ * - D [G][M][N] is FP32 (a weight gradient), D[g] = C[g] + A_g^T B_g with the
+ *   same per-chunk promotion as above, the sum taken in FP64 and rounded once to
+ *   FP32 (nearest even); C may be NULL (zero).  An empty group gives D[g] = C[g]
+ *   (or zeros).
+ *
+ * Returns 0, or -1 when a group size is negative or not a multiple of 128, or the
+ * sizes do not add up to K_total. */
+ORACLE_API int fp8bs_oracle_k_grouped(const uint8_t* A, const float* SA, const uint8_t* B,
+                                      const float* SB, const int64_t* ks, const float* C,
+                                      float* D, int64_t G, int64_t M, int64_t N,
+                                      int64_t K_total) {
+    int64_t g, sum = 0, i;
+    if (G < 1 || M < 1 || N < 1 || K_total < 0 || K_total % 128 != 0) return -1;
+    for (g = 0; g < G; ++g) {
+        if (ks[g] < 0 || ks[g] % 128 != 0) return -1;
+        sum += ks[g];
+    }
+    if (sum != K_total) return -1;
+    init_dec_table();
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < G * M; ++i) {
+        const int64_t kbt = K_total / 128;
+        int64_t gg = i / M, m = i % M, k0 = 0, j, n;
+        for (j = 0; j < gg; ++j) k0 += ks[j];
+        for (n = 0; n < N; ++n) {
+            double v = element_acc(A + k0 * M + m, M, SA + m * kbt + k0 / 128, 1,
+                                   B + k0 * N + n, N, SB + n * kbt + k0 / 128, 1, ks[gg]);
+            if (C) v += (double)C[i * N + n];
+            D[i * N + n] = (float)v;     /* one rounding, nearest even */
+        }
     }
     return 0;
 }

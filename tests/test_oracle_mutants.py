@@ -38,8 +38,22 @@ MUTANTS = {
     "addend_masked_slot_rows": ("if (i % rows >= valid) continue;", "if (i % rows > valid) continue;"),
     "weight_block_skips_last_row": ("int64_t n1 = 128 * i + 128 < N ? 128 * i + 128 : N;",
                                     "int64_t n1 = 128 * i + 127 < N ? 128 * i + 127 : N;"),
+    # stored forms and the K-grouped product
+    "layout_a_step_k": ("const ptrdiff_t a_step = a_transposed ? M : 1;",
+                        "const ptrdiff_t a_step = a_transposed ? K : 1;"),
+    "layout_b_forms_swapped": ("const uint8_t* b = b_transposed ? B + n * K : B + n;",
+                               "const uint8_t* b = b_transposed ? B + n : B + n * K;"),
+    "layout_addend_dropped": ("if (C) v += (double)C[r * N + n];", "(void)C;"),
+    "kgrouped_group_offset": ("for (j = 0; j < gg; ++j) k0 += ks[j];",
+                              "for (j = 0; j + 1 < gg; ++j) k0 += ks[j];"),
+    "kgrouped_b_scale_per_block": ("SB + n * kbt + k0 / 128", "SB + (n / 128) * kbt + k0 / 128"),
+    "kgrouped_a_scale_from_chunk0": ("SA + m * kbt + k0 / 128", "SA + m * kbt"),
+    "kgrouped_truncates": ("D[i * N + n] = (float)v;",
+                           "{ float f = (float)v; if (fabs((double)f) > fabs(v)) "
+                           "f = nextafterf(f, 0.0f); D[i * N + n] = f; }"),
+    "kgrouped_addend_dropped": ("if (C) v += (double)C[i * N + n];", "(void)C;"),
 }
-PIN_FILES = ["test_oracle_pins.py", "test_oracle_quant_pins.py"]
+PIN_FILES = ["test_oracle_pins.py", "test_oracle_quant_pins.py", "test_oracle_layout_pins.py"]
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))

@@ -71,3 +71,31 @@ def test_masked_counts_in_range():
 def test_workload_families_cover_the_shapes():
     n = [len(synth.workload_shapes(i)) for i in range(5)]
     assert n == [1, 6, 9, 2, 2]
+
+
+def test_k_grouped_segments_padding_and_scales():
+    p = synth.make_k_grouped(4, 48, 40, seed=5000, total_tokens=700)
+    assert p.counts.sum() == 700 and np.all(p.ks % 128 == 0)
+    assert np.all(p.ks - p.counts >= 0) and np.all(p.ks - p.counts < 128)
+    K = int(p.ks.sum())
+    assert p.A.shape == (K, 48) and p.B.shape == (K, 40)
+    assert p.SA.shape == (48, K // 128) and p.SB.shape == (40, K // 128)
+    k0 = 0
+    for c, k in zip(p.counts, p.ks):
+        assert np.all(p.A[k0 + c:k0 + k] == 0) and np.all(p.B[k0 + c:k0 + k] == 0)
+        k0 += int(k)
+    # one scale per feature and 128-token chunk: every chunk of a feature with real tokens
+    # reaches the e4m3 maximum once
+    for c in range(K // 128):
+        col = p.A[128 * c:128 * c + 128, :]
+        if np.any(col):
+            assert np.all((col & 0x7F).max(axis=0) == 0x7E)
+    assert [len(synth.workload_shapes(5))] == [2]
+
+
+def test_stored_operands_are_transposes():
+    p = synth.make_dense(40, 70, 256, seed=1)
+    for ab in ("nt", "nn", "tn", "tt"):
+        A, B = synth.stored_operands(p, ab)
+        assert np.array_equal(A if ab[0] == "n" else A.T, p.A)
+        assert np.array_equal(B if ab[1] == "t" else B.T, p.B[0])
