@@ -32,7 +32,9 @@
  *       DG_PRINT_CONFIGS.
  *   - "deepseek开源周第三天：DeepGEMM深度分析", pxiaoer.blog: the FP8 training
  *     list (1x128 activation tiles, 128x128 weight blocks, FP32 accumulation).
- *   The "+ C" term of the pages' naming is available through the _c entry points.
+ *   The "+ C" term of the pages' naming is available through the _c entry points;
+ *   the nn / tn / tt stored forms and the K-grouped weight-gradient GEMM have entry
+ *   points of their own (described next to them).
  *
  * Conventions shared by every entry point:
  *   - All tensor pointers are DEVICE pointers on the current HIP device; the
@@ -78,11 +80,18 @@ typedef enum {
     FP8BS_ERR_HIP = 4           /* the HIP runtime reported an error          */
 } fp8bs_status;
 
-/* Layout codes for the planner queries. */
+/* Layout codes for the planner queries (fp8bs_plan_query, fp8bs_workspace_size,
+ * fp8bs_count_tiles, fp8bs_describe_config).  The first three are the NT entry
+ * points; K_GROUPED is fp8bs_k_grouped_tn_contiguous (m = M, k = K_total, num_groups
+ * groups); DENSE_NN / _TN / _TT are fp8bs_dense_nn / _tn / _tt. */
 typedef enum {
     FP8BS_LAYOUT_DENSE = 0,
     FP8BS_LAYOUT_CONTIGUOUS = 1,
-    FP8BS_LAYOUT_MASKED = 2
+    FP8BS_LAYOUT_MASKED = 2,
+    FP8BS_LAYOUT_K_GROUPED = 3,
+    FP8BS_LAYOUT_DENSE_NN = 4,
+    FP8BS_LAYOUT_DENSE_TN = 5,
+    FP8BS_LAYOUT_DENSE_TT = 6
 } fp8bs_layout;
 
 /*
@@ -214,6 +223,61 @@ int fp8bs_grouped_masked_nt_ue8m0(const void* a, const int32_t* sfa, const void*
                                   int num_groups, int max_m, int expected_m, int n, int k,
                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Dense GEMM with the other stored operand forms ([hada] "Giao diện GEMM và ràng
+ * buộc layout" and "Dense và Grouped GEMM": kernels named for D = C + A @ B, the
+ * two letters saying whether A and B enter as stored or transposed; the newer
+ * architecture accepts nt, tn, nn and tt).  Every tensor is row-major:
+ *   nn:  a e4m3 [m][k],  b e4m3 [k][n]      (D = A B)
+ *   tn:  a e4m3 [k][m],  b e4m3 [k][n]      (D = A^T B)
+ *   tt:  a e4m3 [k][m],  b e4m3 [n][k]      (D = A^T B^T)
+ * The value, the scales (sfa f32 [k/128][fp8bs_get_sfa_ld(m)] MN-major, sfb f32
+ * [ceil(n/128)][k/128]) and D (bf16 [m][n]) are those of fp8bs_dense_nt_c: logical row
+ * r of A and column n of B meet along K whatever their storage.  An operand stored
+ * with M (or N) contiguous is staged in LDS as it lies and its MFMA fragments are read
+ * with gfx950's transpose loads, so no transposed copy is made.
+ * Preconditions on top of the NT ones: a stored [k][m] needs m % 16 == 0, a stored
+ * [k][n] needs n % 16 == 0 (16-byte rows).  c (FP32 [m][n], may not overlap d) and
+ * workspace (split-K, as for the _ws calls) may be NULL.
+ */
+int fp8bs_dense_nn(const void* a, const float* sfa, const void* b, const float* sfb,
+                   const float* c, void* d, int m, int n, int k, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream);
+int fp8bs_dense_tn(const void* a, const float* sfa, const void* b, const float* sfb,
+                   const float* c, void* d, int m, int n, int k, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream);
+int fp8bs_dense_tt(const void* a, const float* sfa, const void* b, const float* sfb,
+                   const float* c, void* d, int m, int n, int k, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * K-grouped GEMM for MoE weight gradients ([hada] "Dense và Grouped GEMM": grouping
+ * along K for the MoE weight backward pass, M and N fixed,
+ * k_grouped_fp8_gemm_tn_contiguous).  Groups run along K: group g owns K rows
+ * [k_g, k_g + ks[g]), k_g = ks[0] + ... + ks[g-1], and
+ *
+ *     D[g][m][n] = fp32( C[g][m][n] + sum over group g's chunks c of
+ *                        P_c(m,n) * SFA(m,c) * SFB(n,c) ),
+ *     P_c(m,n) = sum_{k in [128c, 128c+128)} A[k][m] * B[k][n]
+ *
+ * (the tn form: both operands stored with K outermost, one row per token).
+ *   a    e4m3 [k_total][m]     sfa  f32 [k_total/128][fp8bs_get_sfa_ld(m)]
+ *   b    e4m3 [k_total][n]     sfb  f32 [k_total/128][fp8bs_get_sfa_ld(n)]
+ *        (one scale per feature and 128-token chunk on both sides)
+ *   c    f32 [num_groups][m][n] or NULL (zero); may be the same buffer as d
+ *   d    f32 [num_groups][m][n], every element written
+ *   ks   HOST int32 [num_groups]: tokens per group, each a multiple of 128 (0 allowed:
+ *        D[g] = C[g] or zeros), adding up to k_total; read during the call only.
+ * Preconditions: 1 <= num_groups <= 256; m and n multiples of 16 (>= 16); k_total a
+ * multiple of 128 (0 allowed).  workspace (split-K) may be NULL.  The group sizes are
+ * taken on the host and travel in the kernel arguments, so a captured graph replays
+ * the sizes it was captured with.
+ */
+int fp8bs_k_grouped_tn_contiguous(const void* a, const float* sfa, const void* b,
+                                  const float* sfb, const float* c, float* d, const int32_t* ks,
+                                  int num_groups, int m, int n, int k_total, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
+
 /* Workspace bytes the planner's preferred plan uses for a request on the current
  * device (CU cap respected; `m` as in fp8bs_plan_query).  0 means the best plan
  * splits nothing.  Passing at least this much to a _ws call lets it use that
@@ -313,6 +377,8 @@ typedef struct {
     int kind;           /* 0: A and B tiles staged in LDS, persistent grid;
                            1: B streamed into registers, one workgroup per unit */
     int ue8m0;          /* 1: the instance is also compiled for packed UE8M0 scales */
+    int mn;             /* 1: the instance is also compiled for MN-major operands
+                           (dense nn / tn / tt, K-grouped) */
 } fp8bs_plan;
 
 /*

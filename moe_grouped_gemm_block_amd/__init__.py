@@ -31,10 +31,13 @@ __all__ = [
     "fp8bs_dense_nt_ue8m0", "fp8bs_grouped_contiguous_nt_ue8m0", "fp8bs_grouped_masked_nt_ue8m0",
     "ue8m0_exponents", "pack_ue8m0", "sfa_ue8m0_mn_major", "sfb_ue8m0",
     "fp8bs_dense_nt_c", "fp8bs_grouped_contiguous_nt_c", "fp8bs_grouped_masked_nt_c",
-    "LAYOUT_DENSE", "LAYOUT_CONTIGUOUS", "LAYOUT_MASKED",
+    "fp8bs_dense_nn", "fp8bs_dense_tn", "fp8bs_dense_tt", "fp8bs_k_grouped_tn_contiguous",
+    "LAYOUT_DENSE", "LAYOUT_CONTIGUOUS", "LAYOUT_MASKED", "LAYOUT_K_GROUPED",
+    "LAYOUT_DENSE_NN", "LAYOUT_DENSE_TN", "LAYOUT_DENSE_TT",
 ]
 
 LAYOUT_DENSE, LAYOUT_CONTIGUOUS, LAYOUT_MASKED = 0, 1, 2
+LAYOUT_K_GROUPED, LAYOUT_DENSE_NN, LAYOUT_DENSE_TN, LAYOUT_DENSE_TT = 3, 4, 5, 6
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "lib", "libfp8bs.so")
@@ -53,7 +56,7 @@ class _Plan(ctypes.Structure):
                 ("wg_per_cu", ctypes.c_int), ("stages", ctypes.c_int), ("tiles", ctypes.c_int64),
                 ("grid", ctypes.c_int64), ("raster", ctypes.c_int), ("instance", ctypes.c_int),
                 ("splits", ctypes.c_int), ("workspace_bytes", ctypes.c_int64),
-                ("kind", ctypes.c_int), ("ue8m0", ctypes.c_int)]
+                ("kind", ctypes.c_int), ("ue8m0", ctypes.c_int), ("mn", ctypes.c_int)]
 
 
 def library_path() -> str:
@@ -104,6 +107,9 @@ def _load():
     lib.fp8bs_quantize_1x128.restype = I
     lib.fp8bs_quantize_128x128.argtypes = [P, I, P, P, I, I, I, P]
     lib.fp8bs_quantize_128x128.restype = I
+    for f in ("nn", "tn", "tt"):
+        getattr(lib, "fp8bs_dense_" + f).argtypes = [P, P, P, P, P, P, I, I, I, P, S, P]
+    lib.fp8bs_k_grouped_tn_contiguous.argtypes = [P, P, P, P, P, P, P, I, I, I, I, P, S, P]
     lib.fp8bs_describe_config.argtypes = [I, I64, I, I, I, I, ctypes.c_char_p, ctypes.c_size_t]
     lib.fp8bs_count_tiles.argtypes = [I, I64, I, I, I, I]
     lib.fp8bs_count_tiles.restype = I64
@@ -640,3 +646,78 @@ def fp8bs_grouped_masked_nt_c(a, sfa, b, sfb, c, d, masked_m, expected_m: int = 
                                                int(expected_m), n, k, wp, wb,
                                                ctypes.c_void_p(s.cuda_stream))
     _check(st, "fp8bs_grouped_masked_nt_c")
+
+
+# ---- stored forms nn / tn / tt and the K-grouped (weight-gradient) GEMM --------
+
+def _dense_form(form, a, sfa, b, sfb, c, d, workspace, stream):
+    torch = _torch()
+    a_t, b_t = form[0] == "t", form[1] == "t"
+    if a.dim() != 2 or b.dim() != 2:
+        raise ValueError("a and b must be 2-D")
+    m, k = (a.shape[1], a.shape[0]) if a_t else (a.shape[0], a.shape[1])
+    n, kb_ = (b.shape[0], b.shape[1]) if b_t else (b.shape[1], b.shape[0])
+    if kb_ != k or tuple(d.shape) != (m, n):
+        raise ValueError("shape mismatch between a, b and d")
+    kb = k // 128 if k % 128 == 0 else -1
+    args = (_dev_ptr(a, "a", _fp8_dtypes(), 2), _dev_ptr(sfa, "sfa", (torch.float32,)),
+            _dev_ptr(b, "b", _fp8_dtypes(), 2), _dev_ptr(sfb, "sfb", (torch.float32,)))
+    if kb > 0 and (sfa.numel() != kb * get_sfa_ld(m) or sfb.numel() != ((n + 127) // 128) * kb):
+        raise ValueError("scale tensor sizes do not match the shapes")
+    dp = _dev_ptr(d, "d", _bf16_dtypes(), 2)
+    cp = _addend(c, d) if c is not None else ctypes.c_void_p(None)
+    code = {"nn": LAYOUT_DENSE_NN, "tn": LAYOUT_DENSE_TN, "tt": LAYOUT_DENSE_TT}[form]
+    with torch.cuda.device(a.device):
+        s = _stream(stream, a.device)
+        wp, wb, _keep = _workspace(workspace, code, m, n, k, 1, 0, s, a.device)
+        st = getattr(_load(), "fp8bs_dense_" + form)(*args, cp, dp, m, n, k, wp, wb,
+                                                     ctypes.c_void_p(s.cuda_stream))
+    _check(st, "fp8bs_dense_" + form)
+
+
+def fp8bs_dense_nn(a, sfa, b, sfb, d, c=None, workspace=None, stream=None):
+    """D = bf16(C + A B): a e4m3 [m][k], b e4m3 [k][n] (N contiguous); scales and d as
+    fp8bs_dense_nt; c optional FP32 [m][n]."""
+    _dense_form("nn", a, sfa, b, sfb, c, d, workspace, stream)
+
+
+def fp8bs_dense_tn(a, sfa, b, sfb, d, c=None, workspace=None, stream=None):
+    """D = bf16(C + A^T B): a e4m3 [k][m], b e4m3 [k][n]."""
+    _dense_form("tn", a, sfa, b, sfb, c, d, workspace, stream)
+
+
+def fp8bs_dense_tt(a, sfa, b, sfb, d, c=None, workspace=None, stream=None):
+    """D = bf16(C + A^T B^T): a e4m3 [k][m], b e4m3 [n][k]."""
+    _dense_form("tt", a, sfa, b, sfb, c, d, workspace, stream)
+
+
+def fp8bs_k_grouped_tn_contiguous(a, sfa, b, sfb, d, ks, c=None, workspace=None, stream=None):
+    """K-grouped weight-gradient GEMM: D[g] = C[g] + A_g^T B_g in FP32.
+
+    a: e4m3 [k_total][m]; b: e4m3 [k_total][n]; sfa: f32 [k_total/128][ld(m)];
+    sfb: f32 [k_total/128][ld(n)]; d: f32 [g][m][n] (every element written); ks: the g
+    group sizes along K (a host sequence of ints, multiples of 128 adding up to k_total);
+    c: optional f32 [g][m][n] (may be d itself)."""
+    torch = _torch()
+    sizes = [int(x) for x in ks]
+    g = len(sizes)
+    if a.dim() != 2 or b.dim() != 2 or d.dim() != 3:
+        raise ValueError("a and b must be 2-D, d 3-D")
+    k_total, m = a.shape
+    n = b.shape[1]
+    if b.shape[0] != k_total or tuple(d.shape) != (g, m, n):
+        raise ValueError("shape mismatch between a, b, d and ks")
+    kb = k_total // 128 if k_total % 128 == 0 else -1
+    args = (_dev_ptr(a, "a", _fp8_dtypes(), 2), _dev_ptr(sfa, "sfa", (torch.float32,)),
+            _dev_ptr(b, "b", _fp8_dtypes(), 2), _dev_ptr(sfb, "sfb", (torch.float32,)))
+    if kb >= 0 and (sfa.numel() != kb * get_sfa_ld(m) or sfb.numel() != kb * get_sfa_ld(n)):
+        raise ValueError("scale tensor sizes do not match the shapes")
+    dp = _dev_ptr(d, "d", (torch.float32,), 3)
+    cp = _addend(c, d) if c is not None else ctypes.c_void_p(None)
+    ks_host = (ctypes.c_int32 * max(g, 1))(*sizes)
+    with torch.cuda.device(a.device):
+        s = _stream(stream, a.device)
+        wp, wb, _keep = _workspace(workspace, LAYOUT_K_GROUPED, m, n, k_total, g, 0, s, a.device)
+        st = _load().fp8bs_k_grouped_tn_contiguous(*args, cp, dp, ks_host, g, m, n, k_total,
+                                                   wp, wb, ctypes.c_void_p(s.cuda_stream))
+    _check(st, "fp8bs_k_grouped_tn_contiguous")

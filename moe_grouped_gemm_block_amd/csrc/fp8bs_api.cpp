@@ -44,14 +44,22 @@ int current_num_cus() {
 bool aligned16(const void* p) { return p && ((uintptr_t)p & 15u) == 0; }
 bool aligned4(const void* p) { return p && ((uintptr_t)p & 3u) == 0; }
 
-void format_plan(const fp8bs::Plan& pl, int layout, int64_t m, int n, int k, int g,
+// Names of the public layout codes (FP8BS_LAYOUT_*).
+int layout_code(int layout, int form) {
+    if (layout == fp8bs::kKGrouped) return 3;
+    if (layout == fp8bs::kDense && form != fp8bs::kFormNT) return 3 + form;
+    return layout;
+}
+
+void format_plan(const fp8bs::Plan& pl, int layout, int form, int64_t m, int n, int k, int g,
                  int expected_m, int cus, char* buf, size_t len) {
-    static const char* names[3] = {"dense", "contiguous", "masked"};
+    static const char* names[7] = {"dense", "contiguous", "masked", "k-grouped tn",
+                                   "dense nn", "dense tn", "dense tt"};
     snprintf(buf, len,
              "fp8bs %s m=%lld n=%d k=%d groups=%d expected_m=%d cus=%d -> %s block %dx%d "
              "waves %dx%d threads %d stages %d lds %dB wg/cu %d tiles %lld splits %d "
              "workspace %lldB grid %lld raster %d instance %d",
-             names[layout], (long long)m, n, k, g, expected_m, cus,
+             names[layout_code(layout, form)], (long long)m, n, k, g, expected_m, cus,
              pl.shape.kind == fp8bs::kStreamB ? "stream-B" : "staged", pl.shape.block_m,
              pl.shape.block_n, pl.shape.waves_m, pl.shape.waves_n,
              64 * pl.shape.waves_m * pl.shape.waves_n, pl.shape.stages, pl.shape.lds_bytes,
@@ -61,41 +69,58 @@ void format_plan(const fp8bs::Plan& pl, int layout, int64_t m, int n, int k, int
 
 // Plan for a request on the current device, honouring the test pins.
 int make_plan(int layout, int64_t m, int n, int k, int num_groups, int expected_m,
-              int64_t ws_bytes, int* cus_out, fp8bs::Plan* pl, int scale_mode = fp8bs::kScaleF32) {
+              int64_t ws_bytes, int* cus_out, fp8bs::Plan* pl, int scale_mode = fp8bs::kScaleF32,
+              int form = fp8bs::kFormNT) {
     const int cus = current_num_cus();
     if (cus <= 0) return FP8BS_ERR_HIP;
     *cus_out = cus;
     int st = fp8bs::plan_request(layout, m, n, k, num_groups, expected_m, cus, ws_bytes, pl,
-                                 scale_mode);
+                                 scale_mode, form);
     if (st != FP8BS_OK) return st;
     const int forced = g_forced_instance.load(std::memory_order_relaxed);
     const int splits = ws_bytes > 0 ? g_forced_splits.load(std::memory_order_relaxed) : 1;
     if (forced >= 0 || splits > 0)
         st = fp8bs::plan_instance(forced >= 0 ? forced : pl->instance, splits, layout, m, n, k,
-                                  num_groups, expected_m, cus, ws_bytes, pl, scale_mode);
+                                  num_groups, expected_m, cus, ws_bytes, pl, scale_mode, form);
     return st;
 }
 
+// group_data: contiguous grouped_layout / masked masked_m (device); K-grouped: the host
+// array of group sizes along K.
 int run(int layout, const void* a, const float* sfa, const void* b, const float* sfb, void* d,
         const int32_t* group_data, int64_t m, int n, int k, int num_groups, int expected_m,
         void* ws, size_t ws_bytes, hipStream_t stream, int scale_mode = fp8bs::kScaleF32,
-        const float* c = nullptr, bool want_c = false) {
-    int st = fp8bs::validate_sizes(layout, m, n, k, num_groups);
+        const float* c = nullptr, bool want_c = false, int form = fp8bs::kFormNT) {
+    int st = fp8bs::validate_sizes(layout, m, n, k, num_groups, form);
     if (st != FP8BS_OK) return st;
-    if (!aligned16(a) || !aligned16(sfa) || !aligned16(b) || !aligned16(sfb) || !aligned16(d))
+    const bool kg = layout == fp8bs::kKGrouped;
+    if (kg) {                                    // host-side group sizes
+        if (!group_data) return FP8BS_ERR_POINTER;
+        int64_t total = 0;
+        for (int g = 0; g < num_groups; ++g) {
+            if (group_data[g] < 0 || group_data[g] % 128 != 0) return FP8BS_ERR_SHAPE;
+            total += group_data[g];
+        }
+        if (total != k) return FP8BS_ERR_SHAPE;
+    }
+    // (a K-grouped call with k_total == 0 reads no operand: those pointers may be NULL)
+    const bool operands_read = !(kg && k == 0);
+    if (operands_read &&
+        (!aligned16(a) || !aligned16(sfa) || !aligned16(b) || !aligned16(sfb)))
         return FP8BS_ERR_POINTER;
-    if (layout != fp8bs::kDense && !aligned4(group_data)) return FP8BS_ERR_POINTER;
+    if (!aligned16(d)) return FP8BS_ERR_POINTER;
+    if (layout != fp8bs::kDense && !kg && !aligned4(group_data)) return FP8BS_ERR_POINTER;
     if (ws_bytes > 0 && !aligned16(ws)) return FP8BS_ERR_POINTER;
     if (want_c && !aligned16(c)) return FP8BS_ERR_POINTER;
     if (m == 0) return FP8BS_OK;
     const int64_t ws_cap = ws_bytes > (size_t)INT64_MAX ? INT64_MAX : (int64_t)ws_bytes;
     int cus = 0;
     fp8bs::Plan pl;
-    st = make_plan(layout, m, n, k, num_groups, expected_m, ws_cap, &cus, &pl, scale_mode);
+    st = make_plan(layout, m, n, k, num_groups, expected_m, ws_cap, &cus, &pl, scale_mode, form);
     if (st != FP8BS_OK) return st;
     if (print_configs()) {
         char line[512];
-        format_plan(pl, layout, m, n, k, num_groups, expected_m, cus, line, sizeof line);
+        format_plan(pl, layout, form, m, n, k, num_groups, expected_m, cus, line, sizeof line);
         fprintf(stderr, "%s\n", line);
     }
     fp8bs::GemmParams p;
@@ -119,7 +144,13 @@ int run(int layout, const void* a, const float* sfa, const void* b, const float*
     p.units = (int)(pl.tiles * pl.splits);
     p.ws = pl.splits > 1 ? (float*)ws : nullptr;
     p.c = want_c ? c : nullptr;
-    const int err = fp8bs::launch_instance(pl, layout, scale_mode, p, stream);
+    p.sfb_ld = (int)fp8bs_get_sfa_ld(n);
+    p.kg_chunk0[0] = 0;
+    if (kg) {
+        p.grouped_layout = nullptr;
+        for (int g = 0; g < num_groups; ++g) p.kg_chunk0[g + 1] = p.kg_chunk0[g] + group_data[g] / 128;
+    }
+    const int err = fp8bs::launch_instance(pl, layout, scale_mode, p, stream, form);
     return err == (int)hipSuccess ? FP8BS_OK : FP8BS_ERR_HIP;
 }
 
@@ -221,17 +252,50 @@ int fp8bs_grouped_masked_nt_ue8m0(const void* a, const int32_t* sfa, const void*
                k, num_groups, expected_m, workspace, workspace_bytes, stream, fp8bs::kScaleUE8M0);
 }
 
-int64_t fp8bs_workspace_size(int layout, int64_t m, int n, int k, int num_groups,
+int fp8bs_dense_nn(const void* a, const float* sfa, const void* b, const float* sfb,
+                   const float* c, void* d, int m, int n, int k, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream) {
+    return run(fp8bs::kDense, a, sfa, b, sfb, d, nullptr, m, n, k, 1, 0, workspace,
+               workspace ? workspace_bytes : 0, stream, fp8bs::kScaleF32, c, c != nullptr,
+               fp8bs::kFormNN);
+}
+
+int fp8bs_dense_tn(const void* a, const float* sfa, const void* b, const float* sfb,
+                   const float* c, void* d, int m, int n, int k, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream) {
+    return run(fp8bs::kDense, a, sfa, b, sfb, d, nullptr, m, n, k, 1, 0, workspace,
+               workspace ? workspace_bytes : 0, stream, fp8bs::kScaleF32, c, c != nullptr,
+               fp8bs::kFormTN);
+}
+
+int fp8bs_dense_tt(const void* a, const float* sfa, const void* b, const float* sfb,
+                   const float* c, void* d, int m, int n, int k, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream) {
+    return run(fp8bs::kDense, a, sfa, b, sfb, d, nullptr, m, n, k, 1, 0, workspace,
+               workspace ? workspace_bytes : 0, stream, fp8bs::kScaleF32, c, c != nullptr,
+               fp8bs::kFormTT);
+}
+
+int fp8bs_k_grouped_tn_contiguous(const void* a, const float* sfa, const void* b,
+                                  const float* sfb, const float* c, float* d, const int32_t* ks,
+                                  int num_groups, int m, int n, int k_total, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+    return run(fp8bs::kKGrouped, a, sfa, b, sfb, d, ks, m, n, k_total, num_groups, 0, workspace,
+               workspace ? workspace_bytes : 0, stream, fp8bs::kScaleF32, c, c != nullptr);
+}
+
+int64_t fp8bs_workspace_size(int layout_code, int64_t m, int n, int k, int num_groups,
                              int expected_m) {
-    if (layout < 0 || layout > 2) return -FP8BS_ERR_UNSUPPORTED;
+    int layout, form;
+    if (!fp8bs::decode_layout(layout_code, &layout, &form)) return -FP8BS_ERR_UNSUPPORTED;
     const int g = layout == fp8bs::kDense ? 1 : num_groups;
-    int st = fp8bs::validate_sizes(layout, m, n, k, g);
+    int st = fp8bs::validate_sizes(layout, m, n, k, g, form);
     if (st != FP8BS_OK) return -st;
     if (m == 0) return 0;
     int cus = 0;
     fp8bs::Plan pl;
     // the planner's choice with unlimited workspace, then any pins
-    st = make_plan(layout, m, n, k, g, expected_m, INT64_MAX, &cus, &pl);
+    st = make_plan(layout, m, n, k, g, expected_m, INT64_MAX, &cus, &pl, fp8bs::kScaleF32, form);
     if (st != FP8BS_OK) return -st;
     return pl.workspace_bytes;
 }
@@ -253,19 +317,21 @@ int fp8bs_force_splits(int s) {
     return g_forced_splits.exchange(s);
 }
 
-int fp8bs_describe_config(int layout, int64_t m, int n, int k, int num_groups, int expected_m,
-                          char* buf, size_t len) {
+int fp8bs_describe_config(int layout_code, int64_t m, int n, int k, int num_groups,
+                          int expected_m, char* buf, size_t len) {
     if (!buf || len == 0) return FP8BS_ERR_POINTER;
-    if (layout < 0 || layout > 2) return FP8BS_ERR_UNSUPPORTED;
+    int layout, form;
+    if (!fp8bs::decode_layout(layout_code, &layout, &form)) return FP8BS_ERR_UNSUPPORTED;
     const int g = layout == fp8bs::kDense ? 1 : num_groups;
     int cus = 0;
     fp8bs::Plan pl;
-    const int st = make_plan(layout, m, n, k, g, expected_m, INT64_MAX, &cus, &pl);
+    const int st = make_plan(layout, m, n, k, g, expected_m, INT64_MAX, &cus, &pl,
+                             fp8bs::kScaleF32, form);
     if (st != FP8BS_OK) {
         snprintf(buf, len, "%s", fp8bs_status_string(st));
         return st;
     }
-    format_plan(pl, layout, m, n, k, g, expected_m, cus, buf, len);
+    format_plan(pl, layout, form, m, n, k, g, expected_m, cus, buf, len);
     return FP8BS_OK;
 }
 

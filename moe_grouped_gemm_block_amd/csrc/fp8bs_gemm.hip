@@ -108,6 +108,29 @@ __device__ __forceinline__ int logical_block_id() {
     return (b & 7) * (n >> 3) + (b >> 3);
 }
 
+// LDS transpose read (ds_read_b64_tr_b8, gfx950).  Within each group of 16 lanes, lane s
+// supplies the address of an 8-byte row R_s; lane t receives byte (t % 8) of the rows
+// R_{t/8}, R_{t/8 + 2}, ..., R_{t/8 + 14}, in that order (behaviour measured on MI355X).
+// With lane s pointing at k-row kb + s/2, bytes 8*(s%2) .. +7 of a 16-column run of an
+// MN-major tile, lane t therefore gets column t of the run at k = kb .. kb+7: eight
+// consecutive K values of one operand row, as an MFMA fragment needs them.
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ i32x2_t lds_read_tr8(const uint8_t* p) {
+    return __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS i32x2_t*)(LDS_AS void*)p);
+}
+
+// Swizzle key of k-row `kr` of an MN-major tile with U 16-byte units per row (U = 2 .. 16):
+// physical unit = logical unit ^ key.  A transpose read has each 16-lane group read one
+// logical unit of 8 consecutive k-rows, and the two groups of a half-wavefront rows 32
+// apart; the key spreads those 16 (row, unit) pairs over all 64 banks.  The key of rows
+// 32q + 8r + j (j < 8) depends only on j and q % 2.
+template <int U>
+__device__ __forceinline__ int mn_key(int kr) {
+    static_assert(U == 2 || U == 4 || U == 8 || U == 16, "MN-major tile width");
+    constexpr int ROWS_PER_256B = 16 / U;
+    return ((kr / ROWS_PER_256B) & (U / 2 - 1)) | (((kr >> 5) & 1) * (U / 2));
+}
+
 // LDS swizzle keys (see the fragment-address comment in the kernel).
 __device__ __forceinline__ int b_key(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 template <int TM>
@@ -119,13 +142,13 @@ struct Tile {
     int g, m0, n0, row_limit;
 };
 
-// Schedule position -> tile.  Masked: slot-major.  Within a slot, groups of
+// Schedule position -> tile.  Masked and K-grouped: group-major.  Within a slot, groups of
 // `raster` m-blocks sweep the n-blocks column by column.  Returns false when
 // the tile holds no valid row (masked: beyond masked_m; contiguous: padding).
 template <int BM, int BN, int LAYOUT>
 __device__ __forceinline__ bool tile_at(const GemmParams& p, int t, Tile& tl) {
     int rest = t, g = 0;
-    if (LAYOUT == kMasked) {
+    if (LAYOUT == kMasked || LAYOUT == kKGrouped) {
         const int per_slot = p.m_blocks * p.n_blocks;
         g = t / per_slot;
         rest = t - g * per_slot;
@@ -159,8 +182,17 @@ struct Unit {
     Tile tl;
 };
 
-template <int BM, int BN, int LAYOUT>
-__device__ __forceinline__ bool next_unit(const GemmParams& p, int u, Unit& w) {
+struct NoEmptyUnits {
+    __device__ void operator()(const Unit&) const {}
+};
+
+// The next unit at or after schedule position u (stepping by the grid) that has chunks to
+// multiply.  K-grouped: a unit's chunks are split s of its group's chunks, and a unit
+// with none (an empty group, or more splits than the group has chunks) is handed to
+// on_empty -- which stores its all-zero result -- and skipped.
+template <int BM, int BN, int LAYOUT, typename OnEmpty = NoEmptyUnits>
+__device__ __forceinline__ bool next_unit(const GemmParams& p, int u, Unit& w,
+                                          OnEmpty&& on_empty = OnEmpty{}) {
     const int kchunks = p.k / 128;
     for (; u < p.units; u += gridDim.x) {
         const int s = u / p.tiles, t = u - s * p.tiles;
@@ -168,25 +200,64 @@ __device__ __forceinline__ bool next_unit(const GemmParams& p, int u, Unit& w) {
         w.u = u;
         w.t = t;
         w.s = s;
-        w.c0 = (int)((int64_t)s * kchunks / p.splits);
-        w.c1 = (int)((int64_t)(s + 1) * kchunks / p.splits);
+        if constexpr (LAYOUT == kKGrouped) {
+            const int cb = p.kg_chunk0[w.tl.g];
+            const int nch = p.kg_chunk0[w.tl.g + 1] - cb;
+            w.c0 = cb + (int)((int64_t)s * nch / p.splits);
+            w.c1 = cb + (int)((int64_t)(s + 1) * nch / p.splits);
+            if (w.c0 == w.c1) {
+                on_empty(w);
+                continue;
+            }
+        } else {
+            w.c0 = (int)((int64_t)s * kchunks / p.splits);
+            w.c1 = (int)((int64_t)(s + 1) * kchunks / p.splits);
+        }
         return true;
     }
     return false;
 }
 
-// Rows / columns this lane holds in a tile and the BF16 store of an accumulator set:
+// Rows / columns this lane holds in a tile and the store of an accumulator set:
 // lane (j = l%16, quarter kq = l/16) of wavefront (wm, wn) owns rows
-// m0 + wm*WTM + TM*j + (i ^ flip) and columns n0 + wn*WTN + 16*jn + 4*kq .. +3.
-template <int TM, int TN, int WTM, int WTN, int LAYOUT>
+// m0 + wm*WTM + TM*j + (i ^ flip) (ROWS16: m0 + wm*WTM + 16*i + j, the row order of an
+// MN-major A read by transpose loads) and columns n0 + wn*WTN + 16*jn + 4*kq .. +3.
+// BF16 output; the K-grouped layout stores FP32 into D [G][M][N].
+template <int TM, int TN, int WTM, int WTN, int LAYOUT, bool ROWS16 = false>
 __device__ __forceinline__ void store_tile(const GemmParams& p, const Tile& tl, const f32x4 (&acc)[TM][TN],
                                            int wm, int wn, int lj, int kq, int flip) {
+    if constexpr (LAYOUT == kKGrouped) {
+        const int64_t slot = (int64_t)tl.g * p.m * p.n;
+        float* d_g = (float*)(void*)p.d + slot;
+        const bool vec_ok = (p.n & 3) == 0;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int row = tl.m0 + wm * WTM + (ROWS16 ? 16 * i + lj : TM * lj + (i ^ flip));
+            if (row >= tl.row_limit) continue;
+            float* drow = d_g + (int64_t)row * p.n;
+            const float* crow = p.c ? p.c + slot + (int64_t)row * p.n : nullptr;
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int col = tl.n0 + wn * WTN + 16 * j + 4 * kq;
+                f32x4 v = acc[i][j];
+                if (vec_ok && col + 3 < p.n) {
+                    if (crow) v += *(const f32x4*)(crow + col);
+                    *(f32x4*)(drow + col) = v;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (col + e < p.n) drow[col + e] = crow ? v[e] + crow[col + e] : v[e];
+                }
+            }
+        }
+        return;
+    }
     const int64_t slot = LAYOUT == kMasked ? (int64_t)tl.g * p.m * p.n : (int64_t)0;
     uint16_t* d_g = p.d + slot;
     const bool vec_ok = (p.n & 3) == 0;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-        const int row = tl.m0 + wm * WTM + TM * lj + (i ^ flip);
+        const int row = tl.m0 + wm * WTM + (ROWS16 ? 16 * i + lj : TM * lj + (i ^ flip));
         bool ok = row < tl.row_limit;
         if (LAYOUT == kContiguous && ok) ok = p.grouped_layout[row] == tl.g;
         if (!ok) continue;
@@ -226,14 +297,25 @@ __device__ __forceinline__ int partial_index(int wave, int i, int j, int lane) {
     return ((wave * TM + i) * TN + j) * 64 + lane;
 }
 
-template <int BM, int BN, int WM, int WN, int NS, int LAYOUT, int SCALE>
+template <int BM, int BN, int WM, int WN, int NS, int LAYOUT, int SCALE, bool AMN = false,
+          bool BMN = false>
 __global__ void __launch_bounds__(64 * WM * WN) fp8bs_gemm_kernel(GemmParams p) {
     // SCALE == kScaleF32: FP32 scales, per-chunk promotion on the VALU.
     // SCALE == kScaleUE8M0: power-of-two scales, E8M0 exponents packed four K groups per
     // 32-bit word; the matrix core applies them (v_mfma_scale_*: each operand row's
     // 32-element K blocks multiplied by 2^(e-127)) and accumulates across chunks itself,
     // so there is no promotion step.
+    // AMN / BMN: A stored [K][M] / B stored [K][N] (MN-major).  Such a tile sits in LDS as
+    // 128 k-rows of block_m (block_n) bytes, 16-byte units swizzled by mn_key, and its
+    // fragments are read with transpose loads; an MN-major A's 16-row blocks are 16
+    // consecutive rows (ROWS16 in store_tile).
+    // LAYOUT == kKGrouped: both operands MN-major, per-group K ranges, B scaled per column
+    // (SFB [K_total/128][sfb_ld]), FP32 output.
     constexpr bool E8 = SCALE == kScaleUE8M0;
+    constexpr bool KG = LAYOUT == kKGrouped;
+    static_assert(!KG || (AMN && BMN), "the K-grouped layout has MN-major operands");
+    static_assert(!(AMN || BMN) || (SCALE == kScaleF32 && (LAYOUT == kDense || KG)),
+                  "MN-major operands: dense or K-grouped, FP32 scales");
     constexpr int NW = WM * WN;                      // wavefronts per workgroup
     constexpr int WTM = BM / WM, WTN = BN / WN;      // wavefront sub-tile
     constexpr int TM = WTM / 16, TN = WTN / 16;      // 16x16 blocks per wavefront
@@ -242,7 +324,9 @@ __global__ void __launch_bounds__(64 * WM * WN) fp8bs_gemm_kernel(GemmParams p) 
     static_assert(TM == 1 || TM == 2 || TM == 4 || TM == 8, "row blocks per wavefront");
     static_assert(NS >= 2, "at least two stages");
     constexpr int A_OFF = 0, B_OFF = BM * 128, SA_OFF = (BM + BN) * 128, SB_OFF = SA_OFF + BM * 4;
-    constexpr int STAGE = stage_bytes(BM, BN);
+    constexpr int STAGE = KG ? kgrouped_stage_bytes(BM, BN) : stage_bytes(BM, BN);
+    static_assert(!AMN || (BM >= 32 && BM <= 256 && (BM & (BM - 1)) == 0), "MN-major A tile");
+    static_assert(!BMN || (BN >= 32 && BN <= 256 && (BN & (BN - 1)) == 0), "MN-major B tile");
     constexpr int A_INS = BM / 8, B_INS = BN / 8;    // 1 KB (8 rows) per wavefront copy
     constexpr int A_PER = (A_INS + NW - 1) / NW, B_PER = (B_INS + NW - 1) / NW;
     static_assert(A_INS >= NW && B_INS >= NW, "every wavefront must own at least one A and one B copy");
@@ -275,7 +359,21 @@ __global__ void __launch_bounds__(64 * WM * WN) fp8bs_gemm_kernel(GemmParams p) 
     // Neither key depends on the block index, so block i / j is an immediate offset.
     const int lj = lane & 15;
     const int kq = lane >> 4;                         // 32-byte quarter of the chunk
-    const int flip = (TM > 1) ? (lj >> 3) : 0;
+    const int flip = (TM > 1 && !AMN) ? (lj >> 3) : 0;
+    // MN-major operands: lane (lj, kq) supplies, for its four transpose reads r = 0..3,
+    // k-row 32*kq + 8*r + lj/2 and bytes 8*(lj%2) .. +7 of the block's 16-byte unit; the
+    // unit's swizzle key does not depend on r.
+    const int tr_row = 32 * kq + (lj >> 1);
+    const int a_tr = A_OFF + tr_row * BM + 8 * (lj & 1);
+    const int a_tr_key = [&] {
+        if constexpr (AMN) return mn_key<BM / 16>(tr_row);
+        else return 0;
+    }();
+    const int b_tr = B_OFF + tr_row * BN + 8 * (lj & 1);
+    const int b_tr_key = [&] {
+        if constexpr (BMN) return mn_key<BN / 16>(tr_row);
+        else return 0;
+    }();
     int a_even[2], a_odd[2];                          // row block i at +128*i (even / odd i)
     {
         const int row0 = wm * WTM + TM * lj;
@@ -294,25 +392,48 @@ __global__ void __launch_bounds__(64 * WM * WN) fp8bs_gemm_kernel(GemmParams p) 
 #pragma unroll
         for (int h = 0; h < 2; ++h) b_base[h] = B_OFF + row0 * 128 + (((2 * kq + h) ^ key) << 4);
     }
-    const int sa_rd = SA_OFF + (wm * WTM + TM * lj) * 4;
+    const int sa_rd = SA_OFF + (wm * WTM + (AMN ? lj : TM * lj)) * 4;
 
     // ---- copies: wavefront copy `ins` moves tile rows 8*ins .. 8*ins+7; lane L fills LDS
     // slot L%8 of row 8*ins + L/8 with the global 16-byte unit (slot ^ key(row)) ----
     // The swizzle key of a copied row is the same for rows r and r + 8*NW, so the lane
     // offset of every copy of a tile is one value plus a uniform multiple of 8*NW rows.
-    static_assert((TM == 1 || NW % TM == 0) && NW % 2 == 0, "copy offsets must repeat");
+    static_assert(AMN || (TM == 1 || NW % TM == 0), "copy offsets must repeat");
+    static_assert(NW % 2 == 0, "wavefront count");
     const int cp_row = lane >> 3, cp_slot = lane & 7;
     const uint32_t a_lane = (uint32_t)(8 * wave + cp_row) * (uint32_t)K +
                             (uint32_t)((cp_slot ^ a_key<TM>(8 * wave + cp_row)) << 4);
     const uint32_t b_lane = (uint32_t)(8 * wave + cp_row) * (uint32_t)K +
                             (uint32_t)((cp_slot ^ b_key(8 * wave + cp_row)) << 4);
     // copy chunk c of tile `tl` into stage s
+    // MN-major copy: wavefront copy `ins` fills LDS bytes ins*1024 .. +1023 of the tile,
+    // k-rows of W bytes; lane L's 16 bytes are physical unit (16L % W) / 16 of k-row
+    // (1024 ins + 16L) / W, read from the global row (leading dimension ld) at the
+    // logical unit, clamped to the last whole unit of the row (lim = ld - 16) so that no
+    // read leaves the operand; columns past the edge only feed outputs never stored.
+    auto mn_copy = [&](const uint8_t* chunk, int ld, int lim, int col0, auto w_const, int ins,
+                       LDS_AS void* dst) {
+        constexpr int W = decltype(w_const)::value;
+        const int off = ins * 1024 + 16 * lane;
+        const int kr = off / W;
+        const int u = ((off % W) >> 4) ^ mn_key<W / 16>(kr);
+        const int col = min(col0 + 16 * u, lim);
+        dma16(chunk + (uint32_t)(kr * ld + col), dst);
+    };
     auto issue = [&](const Tile& tl, int c, int s) {
         uint8_t* st = smem + s * STAGE;
         const uint8_t* a_base = p.a + (LAYOUT == kMasked ? (int64_t)tl.g * p.m * K : (int64_t)0) +
                                 (int64_t)c * 128;
-        const uint8_t* b_base = p.b + (int64_t)tl.g * p.n * K + (int64_t)c * 128;
-        if (tl.m0 + BM <= tl.row_limit) {             // whole tile inside: no clamping
+        const uint8_t* b_base = p.b + (KG ? (int64_t)0 : (int64_t)tl.g * p.n * K) + (int64_t)c * 128;
+        if constexpr (AMN) {
+            const uint8_t* a_chunk = p.a + (int64_t)c * 128 * p.m;
+#pragma unroll
+            for (int k = 0; k < A_PER; ++k) {
+                const int kk = (A_INS % NW == 0 || wave + k * NW < A_INS) ? k : k - 1;
+                mn_copy(a_chunk, p.m, p.m - 16, tl.m0, std::integral_constant<int, BM>{},
+                        wave + kk * NW, (LDS_AS void*)(st + A_OFF + (wave + kk * NW) * 1024));
+            }
+        } else if (tl.m0 + BM <= tl.row_limit) {      // whole tile inside: no clamping
             const uint8_t* a_t = a_base + (int64_t)tl.m0 * K;
 #pragma unroll
             for (int k = 0; k < A_PER; ++k) {
@@ -330,7 +451,15 @@ __global__ void __launch_bounds__(64 * WM * WN) fp8bs_gemm_kernel(GemmParams p) 
                 dma16(a_base + off, (LDS_AS void*)(st + A_OFF + ins * 1024));
             }
         }
-        if (tl.n0 + BN <= p.n) {
+        if constexpr (BMN) {
+            const uint8_t* b_chunk = p.b + (int64_t)c * 128 * p.n;
+#pragma unroll
+            for (int k = 0; k < B_PER; ++k) {
+                const int kk = (B_INS % NW == 0 || wave + k * NW < B_INS) ? k : k - 1;
+                mn_copy(b_chunk, p.n, p.n - 16, tl.n0, std::integral_constant<int, BN>{},
+                        wave + kk * NW, (LDS_AS void*)(st + B_OFF + (wave + kk * NW) * 1024));
+            }
+        } else if (tl.n0 + BN <= p.n) {
             const uint8_t* b_t = b_base + (int64_t)tl.n0 * K;
 #pragma unroll
             for (int k = 0; k < B_PER; ++k) {
@@ -359,6 +488,16 @@ __global__ void __launch_bounds__(64 * WM * WN) fp8bs_gemm_kernel(GemmParams p) 
             int r4 = tl.m0 + 4 * lane;                // rows past the scale array are unused
             if (r4 >= p.sfa_ld) r4 = 0;
             if (4 * lane < BM) dma16(sa_base + (uint32_t)r4 * 4u, (LDS_AS void*)(st + SA_OFF));
+        } else if constexpr (KG) {
+            // the tile's block_n per-column B scales of chunk c (MN-major SFB, contiguous);
+            // wavefront NW-2 copies them, the others repeat its first 16 bytes so that
+            // every wavefront issues one copy per chunk
+            const uint8_t* sb_row = (const uint8_t*)(p.sfb + (int64_t)c * p.sfb_ld);
+            int c4 = tl.n0 + 4 * lane;                // columns past the scale row are unused
+            if (c4 >= p.sfb_ld) c4 = 0;
+            const bool mine = wave == NW - 2 ? 4 * lane < BN : lane == 0;
+            if (wave != NW - 2) c4 = tl.n0 < p.sfb_ld ? tl.n0 : 0;
+            if (mine) dma16(sb_row + (uint32_t)c4 * 4u, (LDS_AS void*)(st + SB_OFF));
         } else {
             // the B-scale values of the column blocks the tile touches (every other
             // wavefront writes the same bytes)
@@ -371,16 +510,33 @@ __global__ void __launch_bounds__(64 * WM * WN) fp8bs_gemm_kernel(GemmParams p) 
     };
 
     // ---- LDS fragment and scale readers (stage base `st`) ----
+    // MN-major fragment of the 16-row block whose logical unit is u: four transpose reads,
+    // read r giving the lane's K bytes 32*kq + 8*r .. +7 (the K-major reads' assignment)
+    auto load_tr = [&](const uint8_t* st, int base, int key, int u, auto w_const) {
+        constexpr int W = decltype(w_const)::value;
+        const uint8_t* q = st + base + ((u ^ key) << 4);
+        const i32x2_t r0 = lds_read_tr8(q), r1 = lds_read_tr8(q + 8 * W);
+        const i32x2_t r2 = lds_read_tr8(q + 16 * W), r3 = lds_read_tr8(q + 24 * W);
+        return i32x8{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
+    };
     auto load_a = [&](const uint8_t* st, int i) {
-        const int* base = (i & 1) ? a_odd : a_even;
-        const i32x4 lo = *(const i32x4*)(st + base[0] + 128 * i);
-        const i32x4 hi = *(const i32x4*)(st + base[1] + 128 * i);
-        return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        if constexpr (AMN) {
+            return load_tr(st, a_tr, a_tr_key, wm * TM + i, std::integral_constant<int, BM>{});
+        } else {
+            const int* base = (i & 1) ? a_odd : a_even;
+            const i32x4 lo = *(const i32x4*)(st + base[0] + 128 * i);
+            const i32x4 hi = *(const i32x4*)(st + base[1] + 128 * i);
+            return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
     };
     auto load_b = [&](const uint8_t* st, int j) {
-        const i32x4 lo = *(const i32x4*)(st + b_base[0] + 2048 * j);
-        const i32x4 hi = *(const i32x4*)(st + b_base[1] + 2048 * j);
-        return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        if constexpr (BMN) {
+            return load_tr(st, b_tr, b_tr_key, wn * TN + j, std::integral_constant<int, BN>{});
+        } else {
+            const i32x4 lo = *(const i32x4*)(st + b_base[0] + 2048 * j);
+            const i32x4 hi = *(const i32x4*)(st + b_base[1] + 2048 * j);
+            return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
     };
     // The operand with fewer 16-row blocks stays in registers for the whole chunk; the
     // other is streamed block by block (double buffered).
@@ -394,12 +550,24 @@ __global__ void __launch_bounds__(64 * WM * WN) fp8bs_gemm_kernel(GemmParams p) 
     struct ScaleRegs {
         float sa[TM];
         float sb[UNIFORM_SB ? 1 : TN];
+        f32x4 sbv[KG ? TN : 1];                       // K-grouped: the lane's four columns
     };
     auto load_scales = [&](const uint8_t* st, const Tile& tl, ScaleRegs& r) {
         const float* sap = (const float*)(st + sa_rd);
+        if constexpr (AMN) {
 #pragma unroll
-        for (int i = 0; i < TM; ++i) r.sa[i] = sap[i];
-        if (TM > 1) {
+            for (int i = 0; i < TM; ++i) r.sa[i] = sap[16 * i];
+        } else {
+#pragma unroll
+            for (int i = 0; i < TM; ++i) r.sa[i] = sap[i];
+        }
+        if constexpr (KG) {
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                r.sbv[j] = *(const f32x4*)(st + SB_OFF + (wn * WTN + 16 * j + 4 * kq) * 4);
+            return;
+        }
+        if (TM > 1 && !AMN) {
 #pragma unroll
             for (int i = 0; i < TM; i += 2) {             // this lane's rows are i ^ flip
                 const float x = r.sa[i], y = r.sa[i + 1];
@@ -418,9 +586,30 @@ __global__ void __launch_bounds__(64 * WM * WN) fp8bs_gemm_kernel(GemmParams p) 
         }
     };
 
+    // K-grouped units with no chunk (an empty group, or an empty split of a short one)
+    // store their all-zero result -- D = C, or zeros -- when the compute cursor meets them.
+    auto on_empty = [&](const Unit& w) {
+        if constexpr (KG) {
+            f32x4 z[TM][TN];
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j) z[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (p.splits == 1) {
+                store_tile<TM, TN, WTM, WTN, LAYOUT, AMN>(p, w.tl, z, wm, wn, lj, kq, flip);
+            } else {
+                f32x4* ws = (f32x4*)(p.ws + ((int64_t)w.t * p.splits + w.s) * (BM * BN));
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j) ws[partial_index<TM, TN>(wave, i, j, lane)] = z[i][j];
+            }
+        }
+    };
+
     // ---- the two cursors over this workgroup's (unit, chunk) stream ----
     Unit cur;                                          // the chunk being multiplied
-    if (!next_unit<BM, BN, LAYOUT>(p, logical_block_id(), cur)) return;
+    if (!next_unit<BM, BN, LAYOUT>(p, logical_block_id(), cur, on_empty)) return;
     Unit isu = cur;                                    // the next chunk to copy
     int ic = cur.c0;
     bool live = true;                                  // false: stream exhausted, repeat last
@@ -469,10 +658,17 @@ __global__ void __launch_bounds__(64 * WM * WN) fp8bs_gemm_kernel(GemmParams p) 
         const uint8_t* st = smem + sq * STAGE;
         float sc[TM][UNIFORM_SB ? 1 : TN];
         int sae[E8 ? TM : 1], sbe[E8 ? (UNIFORM_SB ? 1 : TN) : 1];   // E8M0 exponents
+        float kg_sa[KG ? TM : 1];
+        f32x4 kg_sb[KG ? TN : 1];
         {
             ScaleRegs sr;
             load_scales(st, cur.tl, sr);
-            if constexpr (E8) {
+            if constexpr (KG) {
+#pragma unroll
+                for (int i = 0; i < TM; ++i) kg_sa[i] = sr.sa[i];
+#pragma unroll
+                for (int j = 0; j < TN; ++j) kg_sb[j] = sr.sbv[j];
+            } else if constexpr (E8) {
                 const int sh = 8 * (c & 3);             // this chunk's byte of the packed word
 #pragma unroll
                 for (int i = 0; i < TM; ++i) sae[i] = (__builtin_bit_cast(int, sr.sa[i]) >> sh) & 0xFF;
@@ -488,7 +684,10 @@ __global__ void __launch_bounds__(64 * WM * WN) fp8bs_gemm_kernel(GemmParams p) 
         }
         auto promote = [&](int o, int q, const f32x4& part) {
             const int i = STREAM_A ? o : q, j = STREAM_A ? q : o;
-            acc[i][j] += part * sc[i][UNIFORM_SB ? 0 : j];
+            if constexpr (KG)
+                acc[i][j] += (part * kg_sa[i]) * kg_sb[j];  // row scale, then per column
+            else
+                acc[i][j] += part * sc[i][UNIFORM_SB ? 0 : j];
         };
         // Products are issued in the order (o, q), o = streamed block, q = resident block;
         // the result of product k is promoted after product k+LAG has issued, so its
@@ -560,8 +759,8 @@ __global__ void __launch_bounds__(64 * WM * WN) fp8bs_gemm_kernel(GemmParams p) 
             asm volatile("" : "+v"(el));
             if (p.splits == 1) {
                 const int elj = el & 15;
-                store_tile<TM, TN, WTM, WTN, LAYOUT>(p, cur.tl, acc, wm, wn, elj, el >> 4,
-                                                     (TM > 1) ? (elj >> 3) : 0);
+                store_tile<TM, TN, WTM, WTN, LAYOUT, AMN>(p, cur.tl, acc, wm, wn, elj, el >> 4,
+                                                          (TM > 1 && !AMN) ? (elj >> 3) : 0);
             } else {
                 f32x4* ws = (f32x4*)(p.ws + ((int64_t)cur.t * p.splits + cur.s) * (BM * BN));
 #pragma unroll
@@ -573,7 +772,7 @@ __global__ void __launch_bounds__(64 * WM * WN) fp8bs_gemm_kernel(GemmParams p) 
             for (int i = 0; i < TM; ++i)
 #pragma unroll
                 for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (!next_unit<BM, BN, LAYOUT>(p, cur.u + gridDim.x, cur)) break;
+            if (!next_unit<BM, BN, LAYOUT>(p, cur.u + gridDim.x, cur, on_empty)) break;
             c = cur.c0;
         } else {
             ++c;
@@ -844,7 +1043,7 @@ __global__ void __launch_bounds__(64 * NW) fp8bs_stream_kernel(GemmParams p) {
 // are added in split order 0, 1, ..., S-1 (the same order whatever order the splits
 // finished in, so results are reproducible), rounded to BF16 and stored at valid rows
 // and columns exactly as the GEMM kernel's own epilogue would.
-template <int BM, int BN, int WM, int WN, int LAYOUT>
+template <int BM, int BN, int WM, int WN, int LAYOUT, bool AMN = false>
 __global__ void __launch_bounds__(64 * WM * WN) fp8bs_splitk_reduce(GemmParams p) {
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int TM = WTM / 16, TN = WTN / 16;
@@ -852,7 +1051,7 @@ __global__ void __launch_bounds__(64 * WM * WN) fp8bs_splitk_reduce(GemmParams p
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave / WN, wn = wave % WN;
     const int lj = lane & 15, kq = lane >> 4;
-    const int flip = (TM > 1) ? (lj >> 3) : 0;
+    const int flip = (TM > 1 && !AMN) ? (lj >> 3) : 0;
     for (int t = blockIdx.x; t < p.tiles; t += gridDim.x) {
         Tile tl;
         if (!tile_at<BM, BN, LAYOUT>(p, t, tl)) continue;
@@ -869,7 +1068,7 @@ __global__ void __launch_bounds__(64 * WM * WN) fp8bs_splitk_reduce(GemmParams p
 #pragma unroll
                 for (int j = 0; j < TN; ++j) acc[i][j] += wss[partial_index<TM, TN>(wave, i, j, lane)];
         }
-        store_tile<TM, TN, WTM, WTN, LAYOUT>(p, tl, acc, wm, wn, lj, kq, flip);
+        store_tile<TM, TN, WTM, WTN, LAYOUT, AMN>(p, tl, acc, wm, wn, lj, kq, flip);
     }
 }
 
@@ -880,6 +1079,10 @@ struct InstanceEntry {
     KernelFn fn_e8[3];         // packed UE8M0 scales, per layout (null: not compiled)
     KernelFn reduce[3];
     int threads;
+    KernelFn fn_form[4];       // dense, stored forms nt (unused), nn, tn, tt (null: not compiled)
+    KernelFn fn_kg;            // K-grouped
+    KernelFn reduce_amn;       // dense with an MN-major A (tn, tt)
+    KernelFn reduce_kg;
 };
 
 template <int KIND, int BM, int BN, int WM, int WN, int NS, int LAYOUT, int SCALE>
@@ -899,17 +1102,38 @@ constexpr KernelFn e8_fn() {
     else return nullptr;
 }
 
-#define FP8BS_INSTANCE(KIND, BM, BN, WM, WN, NS, OCC, CNS, TNS, SCNS, STNS, E8)            \
+// MN-major variants (staged kernel only): LAYOUT kDense with the form's operand majors, or
+// kKGrouped; REDUCE picks the matching split-K reduction instead.
+template <int KIND, int BM, int BN, int WM, int WN, int NS, int MN, int LAYOUT, bool AMN,
+          bool BMN, bool REDUCE = false>
+constexpr KernelFn mn_fn() {
+    if constexpr (!MN || KIND != kStaged) {
+        return nullptr;
+    } else if constexpr (REDUCE) {
+        return fp8bs_splitk_reduce<BM, BN, WM, WN, LAYOUT, AMN>;
+    } else {
+        return fp8bs_gemm_kernel<BM, BN, WM, WN, NS, LAYOUT, kScaleF32, AMN, BMN>;
+    }
+}
+
+#define FP8BS_INSTANCE(KIND, BM, BN, WM, WN, NS, OCC, CNS, TNS, SCNS, STNS, E8, MN)        \
     {{gemm_fn<KIND, BM, BN, WM, WN, NS, kDense, kScaleF32>(),                              \
       gemm_fn<KIND, BM, BN, WM, WN, NS, kContiguous, kScaleF32>(),                         \
       gemm_fn<KIND, BM, BN, WM, WN, NS, kMasked, kScaleF32>()},                            \
      {e8_fn<KIND, BM, BN, WM, WN, NS, kDense, E8>(),                                       \
       e8_fn<KIND, BM, BN, WM, WN, NS, kContiguous, E8>(),                                  \
       e8_fn<KIND, BM, BN, WM, WN, NS, kMasked, E8>()},                                     \
-     {fp8bs_splitk_reduce<BM, BN, WM, WN, kDense>,                            \
-      fp8bs_splitk_reduce<BM, BN, WM, WN, kContiguous>,                       \
-      fp8bs_splitk_reduce<BM, BN, WM, WN, kMasked>},                          \
-     64 * (WM) * (WN)},
+     {fp8bs_splitk_reduce<BM, BN, WM, WN, kDense>,                                          \
+      fp8bs_splitk_reduce<BM, BN, WM, WN, kContiguous>,                                     \
+      fp8bs_splitk_reduce<BM, BN, WM, WN, kMasked>},                                        \
+     64 * (WM) * (WN),                                                                      \
+     {nullptr,                                                                              \
+      mn_fn<KIND, BM, BN, WM, WN, NS, MN, kDense, false, true>(),                           \
+      mn_fn<KIND, BM, BN, WM, WN, NS, MN, kDense, true, true>(),                            \
+      mn_fn<KIND, BM, BN, WM, WN, NS, MN, kDense, true, false>()},                          \
+     mn_fn<KIND, BM, BN, WM, WN, NS, MN, kKGrouped, true, true>(),                          \
+     mn_fn<KIND, BM, BN, WM, WN, NS, MN, kDense, true, false, true>(),                      \
+     mn_fn<KIND, BM, BN, WM, WN, NS, MN, kKGrouped, true, true, true>()},
 const InstanceEntry kEntries[] = {
 #include "fp8bs_instances.inc"
 };
@@ -918,19 +1142,31 @@ const InstanceEntry kEntries[] = {
 }  // namespace
 
 int launch_instance(const Plan& plan, int layout, int scale_mode, const GemmParams& p,
-                    hipStream_t stream) {
+                    hipStream_t stream, int form) {
     if (plan.instance < 0 || plan.instance >= (int)(sizeof(kEntries) / sizeof(kEntries[0])))
         return (int)hipErrorInvalidValue;
+    if (layout < kDense || layout > kKGrouped || form < kFormNT || form > kFormTT)
+        return (int)hipErrorInvalidValue;
     const InstanceEntry& e = kEntries[plan.instance];
-    const KernelFn fn = scale_mode == kScaleUE8M0 ? e.fn_e8[layout] : e.fn[layout];
-    if (!fn) return (int)hipErrorInvalidValue;
+    KernelFn fn, reduce;
+    if (layout == kKGrouped) {
+        fn = scale_mode == kScaleF32 ? e.fn_kg : nullptr;
+        reduce = e.reduce_kg;
+    } else if (form != kFormNT) {
+        fn = (layout == kDense && scale_mode == kScaleF32) ? e.fn_form[form] : nullptr;
+        reduce = form_a_mn(form) ? e.reduce_amn : e.reduce[kDense];
+    } else {
+        fn = scale_mode == kScaleUE8M0 ? e.fn_e8[layout] : e.fn[layout];
+        reduce = e.reduce[layout];
+    }
+    if (!fn || !reduce) return (int)hipErrorInvalidValue;
     GemmParams args = p;
     void* argv[] = {&args};
     hipError_t err = hipLaunchKernel((const void*)fn, dim3((unsigned)plan.grid),
                                      dim3(e.threads), argv, 0, stream);
     if (err != hipSuccess || p.splits == 1) return (int)err;
     // one workgroup per tile (tiles without valid rows return at once)
-    return (int)hipLaunchKernel((const void*)e.reduce[layout], dim3((unsigned)p.tiles),
+    return (int)hipLaunchKernel((const void*)reduce, dim3((unsigned)p.tiles),
                                 dim3(e.threads), argv, 0, stream);
 }
 

@@ -7,7 +7,18 @@
 
 namespace fp8bs {
 
-enum Layout : int { kDense = 0, kContiguous = 1, kMasked = 2 };
+// kKGrouped: groups run along K (MoE weight gradients): A [K_total][M], B [K_total][N],
+// per-group K ranges, FP32 output D [G][M][N].
+enum Layout : int { kDense = 0, kContiguous = 1, kMasked = 2, kKGrouped = 3 };
+
+// Stored forms of the dense operands: whether A is [M][K] ("n") or [K][M] ("t") and B is
+// [N][K] ("t") or [K][N] ("n").  kFormNT is the K-major form every layout supports.
+enum Form : int { kFormNT = 0, kFormNN = 1, kFormTN = 2, kFormTT = 3 };
+constexpr bool form_a_mn(int form) { return form == kFormTN || form == kFormTT; }
+constexpr bool form_b_mn(int form) { return form == kFormNN || form == kFormTN; }
+
+// Most groups a K-grouped launch takes (their K offsets travel in the kernel arguments).
+constexpr int kMaxKGroups = 256;
 
 // Kernel families.
 //   kStaged: A and B tiles both staged in LDS (direct-to-LDS copies), persistent grid;
@@ -37,12 +48,17 @@ struct InstanceShape {
     int stream_chunk_ns; // the same two when the operands stream from HBM (few rows)
     int stream_tile_ns;
     int ue8m0;           // 1: also compiled for packed UE8M0 scales
+    int mn;              // 1: also compiled for MN-major operands (nn / tn / tt, K-grouped)
 };
 
 // LDS bytes of one pipeline stage: the A tile, the B tile (128 K bytes per
 // row), the tile's block_m A scales and up to 64 B-scale values.
 constexpr int stage_bytes(int block_m, int block_n) {
     return (block_m + block_n) * 128 + block_m * 4 + 256;
+}
+// The K-grouped layout scales B per column: block_n B-scale values per stage.
+constexpr int kgrouped_stage_bytes(int block_m, int block_n) {
+    return (block_m + block_n) * 128 + block_m * 4 + (block_n * 4 > 256 ? block_n * 4 : 256);
 }
 // kStreamB: one stage holds the A tile, its A scales (at least 256 bytes: one per lane of
 // a copy instruction) and 256 bytes of B scales.
@@ -78,6 +94,10 @@ struct GemmParams {
     int units;          // tiles x splits
     float* ws;          // splits > 1: FP32 partial tiles, [tile][split][block_m*block_n]
     const float* c;     // optional FP32 addend with D's shape (nullptr: none)
+    // K-grouped only: leading dimension of the MN-major SFB, and the first 128-K chunk of
+    // each group (kg_chunk0[g] .. kg_chunk0[g+1]-1 are group g's chunks)
+    int sfb_ld;
+    int kg_chunk0[kMaxKGroups + 1];
 };
 
 struct Plan {
@@ -97,22 +117,28 @@ int64_t split_workspace_bytes(const InstanceShape& shape, int64_t tiles, int spl
 // caller offers at least that much workspace) and launch shape.
 // Returns FP8BS_OK or an error status.  No device access.
 int plan_request(int layout, int64_t m, int n, int k, int num_groups, int expected_m,
-                 int num_cus, int64_t workspace_bytes, Plan* out, int scale_mode = kScaleF32);
+                 int num_cus, int64_t workspace_bytes, Plan* out, int scale_mode = kScaleF32,
+                 int form = kFormNT);
 
 // Launch shape for a given instance and split count (used when either is pinned;
 // splits < 1 picks the best split count for the instance within the workspace).
 int plan_instance(int instance, int splits, int layout, int64_t m, int n, int k, int num_groups,
                   int expected_m, int num_cus, int64_t workspace_bytes, Plan* out,
-                  int scale_mode = kScaleF32);
+                  int scale_mode = kScaleF32, int form = kFormNT);
 
 // Copies a plan into the public struct.
 void export_plan(const Plan& p, fp8bs_plan* out);
 
-// Validates sizes for an entry point (FP8BS_OK or FP8BS_ERR_SHAPE).
-int validate_sizes(int layout, int64_t m, int n, int k, int num_groups);
+// Validates sizes for an entry point (FP8BS_OK or FP8BS_ERR_SHAPE).  K-grouped: k is
+// K_total (0 allowed); MN-major operands need their M / N to be a multiple of 16.
+int validate_sizes(int layout, int64_t m, int n, int k, int num_groups, int form = kFormNT);
 
-// Launches instance `plan.instance` for `layout` and scale format; returns a hipError_t value.
+// Public layout code (FP8BS_LAYOUT_*) -> internal layout and stored form; false if unknown.
+bool decode_layout(int code, int* layout, int* form);
+
+// Launches instance `plan.instance` for `layout`, scale format and stored form; returns a
+// hipError_t value.
 int launch_instance(const Plan& plan, int layout, int scale_mode, const GemmParams& p,
-                    hipStream_t stream);
+                    hipStream_t stream, int form = kFormNT);
 
 }  // namespace fp8bs

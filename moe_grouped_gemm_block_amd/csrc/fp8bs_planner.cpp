@@ -16,15 +16,41 @@
 
 namespace fp8bs {
 
-#define FP8BS_INSTANCE(KIND, BM, BN, WM, WN, NS, OCC, CNS, TNS, SCNS, STNS, E8) \
-    {KIND, BM, BN, WM, WN, NS, OCC, instance_lds_bytes(KIND, BM, BN, NS), CNS, TNS, SCNS, STNS, E8},
+#define FP8BS_INSTANCE(KIND, BM, BN, WM, WN, NS, OCC, CNS, TNS, SCNS, STNS, E8, MN) \
+    {KIND, BM, BN, WM, WN, NS, OCC, instance_lds_bytes(KIND, BM, BN, NS), CNS, TNS, SCNS, STNS, E8, MN},
 const InstanceShape kInstances[] = {
 #include "fp8bs_instances.inc"
 };
 #undef FP8BS_INSTANCE
 const int kNumInstances = (int)(sizeof(kInstances) / sizeof(kInstances[0]));
 
-int validate_sizes(int layout, int64_t m, int n, int k, int num_groups) {
+bool decode_layout(int code, int* layout, int* form) {
+    static const int table[7][2] = {{kDense, kFormNT},     {kContiguous, kFormNT},
+                                    {kMasked, kFormNT},    {kKGrouped, kFormTN},
+                                    {kDense, kFormNN},     {kDense, kFormTN},
+                                    {kDense, kFormTT}};
+    if (code < 0 || code > 6) return false;
+    *layout = table[code][0];
+    *form = table[code][1];
+    return true;
+}
+
+int validate_sizes(int layout, int64_t m, int n, int k, int num_groups, int form) {
+    if (layout == kKGrouped) {
+        // A [K_total][M], B [K_total][N]: MN-major rows are copied in 16-byte units
+        if (k < 0 || k % 128 != 0) return FP8BS_ERR_SHAPE;
+        if (m < 16 || m % 16 != 0 || n < 16 || n % 16 != 0) return FP8BS_ERR_SHAPE;
+        if (num_groups < 1 || num_groups > kMaxKGroups) return FP8BS_ERR_SHAPE;
+        if (m > (int64_t)0x7fffffff || (double)m * 128 * 2 >= 4294967296.0 ||
+            (double)n * 128 * 2 >= 4294967296.0)
+            return FP8BS_ERR_SHAPE;
+        if ((double)num_groups * m * n * 4.0 > 4.0e18 || (double)k * (m + n) > 4.0e18)
+            return FP8BS_ERR_SHAPE;
+        return FP8BS_OK;
+    }
+    if (form != kFormNT && layout != kDense) return FP8BS_ERR_UNSUPPORTED;
+    if (form_a_mn(form) && m % 16 != 0) return FP8BS_ERR_SHAPE;
+    if (form_b_mn(form) && n % 16 != 0) return FP8BS_ERR_SHAPE;
     if (k < 128 || k % 128 != 0) return FP8BS_ERR_SHAPE;
     if (n < 1 || m < 0) return FP8BS_ERR_SHAPE;
     if (layout == kContiguous && m % 128 != 0) return FP8BS_ERR_SHAPE;
@@ -62,6 +88,7 @@ namespace {
 
 struct Request {
     int layout;
+    int form;
     int64_t m;
     int n, k, G;
     int64_t eff_rows;    // rows per group the estimate assumes
@@ -71,9 +98,10 @@ struct Request {
 };
 
 Request make_request(int layout, int64_t m, int n, int k, int num_groups, int expected_m,
-                     int num_cus, int64_t workspace_bytes) {
+                     int num_cus, int64_t workspace_bytes, int form) {
     Request r;
     r.layout = layout;
+    r.form = layout == kKGrouped ? kFormTN : form;
     r.m = m;
     r.n = n;
     r.k = k;
@@ -93,18 +121,29 @@ Request make_request(int layout, int64_t m, int n, int k, int num_groups, int ex
 int64_t tile_count(const Request& r, const InstanceShape& s) {
     const int64_t m_blocks = (r.m + s.block_m - 1) / s.block_m;
     const int64_t n_blocks = ((int64_t)r.n + s.block_n - 1) / s.block_n;
-    return (r.layout == kMasked ? r.G : 1) * m_blocks * n_blocks;
+    return (r.layout == kMasked || r.layout == kKGrouped ? r.G : 1) * m_blocks * n_blocks;
 }
 
 bool instance_fits(const Request& r, const InstanceShape& s) {
+    // MN-major operands (nn / tn / tt, K-grouped) need an instance compiled for them
+    if ((r.form != kFormNT || r.layout == kKGrouped) && !s.mn) return false;
     // a contiguous-layout tile must not straddle two 128-row expert blocks
     return !(r.layout == kContiguous && 128 % s.block_m != 0);
 }
 
 // Estimated time of instance s with `splits` K splits; < 0 when infeasible.
 double estimate(const Request& r, const InstanceShape& s, int splits) {
-    const int kchunks = r.k / 128;
-    if (splits < 1 || splits > kchunks) return -1.0;
+    // K-grouped: a tile's chunks are its group's, on average K_total / 128 / G
+    const bool kg = r.layout == kKGrouped;
+    int kchunks = r.k / 128;
+    if (kg) {
+        kchunks = (kchunks + r.G - 1) / r.G;
+        if (kchunks < 1) kchunks = 1;
+    }
+    // (K-grouped: any split count up to the total chunk count runs -- splits beyond a
+    // group's chunks are empty units -- but the estimate uses the mean group)
+    const int max_splits = kg ? (r.k / 128 > 1 ? r.k / 128 : 1) : kchunks;
+    if (splits < 1 || splits > max_splits) return -1.0;
     const int64_t tiles = tile_count(r, s);
     // unit indices (and unit + grid) stay well inside int
     if (tiles * splits > 0x7f000000) return -1.0;
@@ -117,7 +156,7 @@ double estimate(const Request& r, const InstanceShape& s, int splits) {
         sum += (double)rest * (full + 1);
         eff_m_blocks = sum / r.spread;
     }
-    const double eff_tiles = (r.layout == kMasked ? r.G : 1) * eff_m_blocks * n_blocks;
+    const double eff_tiles = (r.layout == kMasked || kg ? r.G : 1) * eff_m_blocks * n_blocks;
     const int64_t units = tiles * splits;
     const int64_t per_cu = (units + r.num_cus - 1) / r.num_cus;
     const int64_t chunks_per_unit = (kchunks + splits - 1) / splits;
@@ -132,8 +171,9 @@ double estimate(const Request& r, const InstanceShape& s, int splits) {
     // down unevenly as they miss in L2); measured, they lose to the B-streaming kernel
     // unless the model favours them by a wide margin.
     if (streaming && s.kind == kStaged) t *= kStagedStreamingBias;
-    double bytes = (double)r.G * r.eff_rows * r.k + (double)r.G * r.n * r.k +
-                   (double)r.G * r.eff_rows * r.n * 2;
+    const double d_bytes = (double)r.G * r.eff_rows * r.n * (kg ? 4 : 2);
+    double bytes = kg ? (double)r.k * (r.m + r.n) + d_bytes
+                      : (double)r.G * r.eff_rows * r.k + (double)r.G * r.n * r.k + d_bytes;
     const double partial_bytes = splits > 1 ? eff_tiles * splits * s.block_m * s.block_n * 4.0 : 0.0;
     bytes += 2.0 * partial_bytes;
     const double t_hbm = bytes / kHbmBytesPerNs;
@@ -142,8 +182,7 @@ double estimate(const Request& r, const InstanceShape& s, int splits) {
     const double fill = (eff_units < r.num_cus ? eff_units : (double)r.num_cus) / r.num_cus;
     t *= 1.0 + 0.1 * (1.0 - fill);
     if (splits > 1)
-        t += kReduceFixedNs +
-             (partial_bytes + (double)r.G * r.eff_rows * r.n * 2) / kReduceBytesPerNs;
+        t += kReduceFixedNs + (partial_bytes + d_bytes) / kReduceBytesPerNs;
     return t;
 }
 
@@ -158,6 +197,7 @@ void fill_launch(int i, const Request& r, int splits, Plan* out) {
     if (grid < 1) grid = 1;
     out->instance = i;
     out->shape = s;
+    if (r.layout == kKGrouped) out->shape.lds_bytes = s.stages * kgrouped_stage_bytes(s.block_m, s.block_n);
     out->tiles = tiles;
     out->grid = grid;
     const int64_t raster = m_blocks < 8 ? m_blocks : 8;
@@ -170,12 +210,14 @@ void fill_launch(int i, const Request& r, int splits, Plan* out) {
 
 int plan_instance(int instance, int splits, int layout, int64_t m, int n, int k, int num_groups,
                   int expected_m, int num_cus, int64_t workspace_bytes, Plan* out,
-                  int scale_mode) {
+                  int scale_mode, int form) {
     if (instance < 0 || instance >= kNumInstances || num_cus < 1) return FP8BS_ERR_UNSUPPORTED;
-    const Request r = make_request(layout, m, n, k, num_groups, expected_m, num_cus, workspace_bytes);
+    const Request r = make_request(layout, m, n, k, num_groups, expected_m, num_cus,
+                                   workspace_bytes, form);
     const InstanceShape& s = kInstances[instance];
     if (!instance_fits(r, s)) return FP8BS_ERR_UNSUPPORTED;
-    if (scale_mode == kScaleUE8M0 && !s.ue8m0) return FP8BS_ERR_UNSUPPORTED;
+    if (scale_mode == kScaleUE8M0 && (!s.ue8m0 || r.form != kFormNT || layout == kKGrouped))
+        return FP8BS_ERR_UNSUPPORTED;
     int best_s = -1;
     if (splits >= 1) {
         if (estimate(r, s, splits) < 0) return FP8BS_ERR_UNSUPPORTED;
@@ -196,11 +238,14 @@ int plan_instance(int instance, int splits, int layout, int64_t m, int n, int k,
 }
 
 int plan_request(int layout, int64_t m, int n, int k, int num_groups, int expected_m,
-                 int num_cus, int64_t workspace_bytes, Plan* out, int scale_mode) {
-    int st = validate_sizes(layout, m, n, k, layout == kDense ? 1 : num_groups);
+                 int num_cus, int64_t workspace_bytes, Plan* out, int scale_mode, int form) {
+    int st = validate_sizes(layout, m, n, k, layout == kDense ? 1 : num_groups, form);
     if (st != FP8BS_OK) return st;
     if (num_cus < 1) return FP8BS_ERR_UNSUPPORTED;
-    const Request r = make_request(layout, m, n, k, num_groups, expected_m, num_cus, workspace_bytes);
+    if (scale_mode == kScaleUE8M0 && (form != kFormNT || layout == kKGrouped))
+        return FP8BS_ERR_UNSUPPORTED;
+    const Request r = make_request(layout, m, n, k, num_groups, expected_m, num_cus,
+                                   workspace_bytes, form);
     double best_t = 0;
     int best = -1, best_s = 1;
     for (int i = 0; i < kNumInstances; ++i) {
@@ -240,30 +285,35 @@ void export_plan(const Plan& p, fp8bs_plan* out) {
     out->workspace_bytes = p.workspace_bytes;
     out->kind = p.shape.kind;
     out->ue8m0 = p.shape.ue8m0;
+    out->mn = p.shape.mn;
 }
 
 }  // namespace fp8bs
 
-extern "C" int fp8bs_plan_query(int layout, int64_t m, int n, int k, int num_groups,
+extern "C" int fp8bs_plan_query(int layout_code, int64_t m, int n, int k, int num_groups,
                                 int expected_m, int num_cus, int64_t workspace_bytes,
                                 fp8bs_plan* out) {
     if (!out) return FP8BS_ERR_POINTER;
-    if (layout < 0 || layout > 2) return FP8BS_ERR_UNSUPPORTED;
+    int layout, form;
+    if (!fp8bs::decode_layout(layout_code, &layout, &form)) return FP8BS_ERR_UNSUPPORTED;
     fp8bs::Plan p;
-    int st = fp8bs::plan_request(layout, m, n, k, layout == 0 ? 1 : num_groups, expected_m,
-                                 num_cus, workspace_bytes, &p);
+    int st = fp8bs::plan_request(layout, m, n, k, layout == fp8bs::kDense ? 1 : num_groups,
+                                 expected_m, num_cus, workspace_bytes, &p, fp8bs::kScaleF32, form);
     if (st != FP8BS_OK) return st;
     fp8bs::export_plan(p, out);
     return FP8BS_OK;
 }
 
-extern "C" int64_t fp8bs_count_tiles(int layout, int64_t m, int n, int num_groups, int block_m,
-                                     int block_n) {
-    if (layout < 0 || layout > 2 || m < 0 || n < 1 || block_m < 1 || block_n < 1) return -1;
-    if (layout == fp8bs::kMasked && num_groups < 1) return -1;
+extern "C" int64_t fp8bs_count_tiles(int layout_code, int64_t m, int n, int num_groups,
+                                     int block_m, int block_n) {
+    int layout, form;
+    if (!fp8bs::decode_layout(layout_code, &layout, &form)) return -1;
+    if (m < 0 || n < 1 || block_m < 1 || block_n < 1) return -1;
+    const bool per_group = layout == fp8bs::kMasked || layout == fp8bs::kKGrouped;
+    if (per_group && num_groups < 1) return -1;
     const int64_t mb = (m + block_m - 1) / block_m;
     const int64_t nb = ((int64_t)n + block_n - 1) / block_n;
-    return (layout == fp8bs::kMasked ? num_groups : 1) * mb * nb;
+    return (per_group ? num_groups : 1) * mb * nb;
 }
 
 extern "C" int fp8bs_num_instances(void) { return fp8bs::kNumInstances; }
@@ -283,7 +333,9 @@ extern "C" const char* fp8bs_status_string(int status) {
     switch (status) {
         case FP8BS_OK: return "ok";
         case FP8BS_ERR_SHAPE: return "invalid shape (K must be a positive multiple of 128, "
-                                     "m_total a multiple of 128, sizes positive)";
+                                     "m_total a multiple of 128, sizes positive; MN-major "
+                                     "operands: M / N multiples of 16; K-grouped: group sizes "
+                                     "multiples of 128 adding up to K_total, at most 256 groups)";
         case FP8BS_ERR_POINTER: return "NULL or misaligned (not 16-byte) pointer";
         case FP8BS_ERR_UNSUPPORTED: return "no compiled kernel instance covers the request "
                                            "(or a pinned instance / split count does not fit it)";

@@ -204,3 +204,58 @@ def test_workspace_size_reports_errors_as_negated_status():
     assert lib.fp8bs_workspace_size(0, 64, 256, 100, 1, 0) == -ERR_SHAPE
     assert lib.fp8bs_workspace_size(7, 64, 256, 128, 1, 0) == -ERR_UNSUPPORTED
     assert lib.fp8bs_workspace_size(0, 0, 256, 128, 1, 0) == 0
+
+
+def test_stored_forms_and_k_grouped_plans():
+    """The nn / tn / tt and K-grouped layout codes plan onto instances compiled for
+    MN-major operands, refuse sizes their copies cannot address, and count tiles per
+    group for the K-grouped layout."""
+    mn = {i["instance"] for i in fp8bs.instances() if i["mn"]}
+    assert mn and all(not i["mn"] or (i["kind"] == 0 and i["block_n"] <= 256 and
+                                      (i["block_m"] & (i["block_m"] - 1)) == 0 and
+                                      (i["block_n"] & (i["block_n"] - 1)) == 0)
+                      for i in fp8bs.instances())
+    for code in (fp8bs.LAYOUT_DENSE_NN, fp8bs.LAYOUT_DENSE_TN, fp8bs.LAYOUT_DENSE_TT):
+        for m, n, k in [(4096, 7168, 7168), (64, 7168, 2048), (256, 4096, 7168)]:
+            p = fp8bs.plan_query(code, m, n, k, workspace_bytes=1 << 30, num_cus=256)
+            assert p["instance"] in mn
+    p = fp8bs.plan_query(fp8bs.LAYOUT_K_GROUPED, 4096, 7168, 32768, 8, num_cus=256)
+    assert p["instance"] in mn
+    assert p["tiles"] == 8 * (4096 // p["block_m"]) * (7168 // p["block_n"])
+    assert fp8bs.count_tiles(fp8bs.LAYOUT_K_GROUPED, 4096, 7168, 8, 256, 256) == 8 * 16 * 28
+    # K-grouped: k_total 0 is a valid request (every group empty)
+    fp8bs.plan_query(fp8bs.LAYOUT_K_GROUPED, 64, 64, 0, 2, num_cus=256)
+    for bad in [(fp8bs.LAYOUT_DENSE_TN, 40, 64, 128), (fp8bs.LAYOUT_DENSE_NN, 64, 40, 128),
+                (fp8bs.LAYOUT_DENSE_TT, 40, 64, 128)]:
+        with pytest.raises(fp8bs.FP8BSError):
+            fp8bs.plan_query(*bad, num_cus=256)
+    fp8bs.plan_query(fp8bs.LAYOUT_DENSE_TT, 48, 40, 128, num_cus=256)   # tt: n free
+    for m, n, k, g in [(40, 64, 256, 2), (64, 40, 256, 2), (64, 64, 200, 2), (64, 64, 256, 0),
+                       (64, 64, 256, 257)]:
+        with pytest.raises(fp8bs.FP8BSError):
+            fp8bs.plan_query(fp8bs.LAYOUT_K_GROUPED, m, n, k, g, num_cus=256)
+    with pytest.raises(fp8bs.FP8BSError):
+        fp8bs.plan_query(7, 64, 64, 128, num_cus=256)
+
+
+def test_stored_form_and_k_grouped_entry_points_validate_before_launching():
+    lib = fp8bs._load()
+    f = _Fake().ptr
+    for name in ("fp8bs_dense_nn", "fp8bs_dense_tn", "fp8bs_dense_tt"):
+        fn = getattr(lib, name)
+        assert fn(f, f, f, f, None, f, 64, 64, 100, None, 0, None) == ERR_SHAPE
+        assert fn(None, f, f, f, None, f, 64, 64, 128, None, 0, None) == ERR_POINTER
+        assert fn(f, f, f, f, f + 4, f, 64, 64, 128, None, 0, None) == ERR_POINTER   # c
+        assert fn(f, f, f, f, None, f, 0, 64, 128, None, 0, None) == OK
+    assert lib.fp8bs_dense_tn(f, f, f, f, None, f, 40, 64, 128, None, 0, None) == ERR_SHAPE
+    assert lib.fp8bs_dense_nn(f, f, f, f, None, f, 64, 40, 128, None, 0, None) == ERR_SHAPE
+    kg = lib.fp8bs_k_grouped_tn_contiguous
+    ks = (ctypes.c_int32 * 3)(128, 0, 256)
+    assert kg(f, f, f, f, None, f, ks, 3, 64, 64, 256, None, 0, None) == ERR_SHAPE   # sum 384
+    bad = (ctypes.c_int32 * 3)(128, 64, 192)
+    assert kg(f, f, f, f, None, f, bad, 3, 64, 64, 384, None, 0, None) == ERR_SHAPE
+    neg = (ctypes.c_int32 * 3)(512, -128, 0)
+    assert kg(f, f, f, f, None, f, neg, 3, 64, 64, 384, None, 0, None) == ERR_SHAPE
+    assert kg(f, f, f, f, None, f, None, 3, 64, 64, 384, None, 0, None) == ERR_POINTER
+    assert kg(f, f, f, f, None, f, ks, 3, 40, 64, 384, None, 0, None) == ERR_SHAPE
+    assert kg(f, f, f, f, None, None, ks, 3, 64, 64, 384, None, 0, None) == ERR_POINTER
