@@ -33,6 +33,9 @@ FAMILY_NAMES = {
     2: "dense decode sweep M in {64,128,256} x (N,K) in {(7168,7168),(7168,2048),(4096,7168)}",
     3: "MoE contiguous G=8, multinomial rows ~32768, (N,K) in {(4096,7168),(7168,2048)}",
     4: "MoE masked G=16, max_m=256, masked_m~U{1..256}, (N,K) in {(4096,7168),(7168,2048)}",
+    5: "MoE K-grouped weight gradients G=8, tokens ~ Multinomial(32768) padded to 128 per "
+       "group, (M,N) in {(4096,7168),(7168,2048)}, FP32 D",
+    6: "dense stored forms nn, tn, tt at M=4096 N=4096 K=7168",
 }
 
 
@@ -115,6 +118,31 @@ def main():
     problems = []
     for desc in synth.workload_shapes(args.family):
         p = synth.make(desc)
+        if p.kind == "k_grouped":
+            ws = torch.empty(max(fp8bs.workspace_size(fp8bs.LAYOUT_K_GROUPED, p.M, p.N, p.K, p.G),
+                                 16), dtype=torch.uint8, device=dev)
+            problems.append(dict(
+                desc=desc, p=p, a=torch.from_numpy(p.A).to(dev),
+                sfa=fp8bs.sfa_mn_major(torch.from_numpy(p.SA)).to(dev),
+                b=torch.from_numpy(p.B).to(dev),
+                sfb=fp8bs.sfa_mn_major(torch.from_numpy(p.SB)).to(dev),
+                d=torch.empty((p.G, p.M, p.N), dtype=torch.float32, device=dev),
+                extra=[int(x) for x in p.ks], ws=ws))
+            continue
+        form = desc.get("form", "nt")
+        if form != "nt":
+            A_st, B_st = synth.stored_operands(p, form)
+            code = {"nn": fp8bs.LAYOUT_DENSE_NN, "tn": fp8bs.LAYOUT_DENSE_TN,
+                    "tt": fp8bs.LAYOUT_DENSE_TT}[form]
+            ws = torch.empty(max(fp8bs.workspace_size(code, p.M, p.N, p.K), 16),
+                             dtype=torch.uint8, device=dev)
+            problems.append(dict(
+                desc=desc, p=p, a=torch.from_numpy(A_st).to(dev),
+                sfa=fp8bs.sfa_mn_major(torch.from_numpy(p.SA)).to(dev),
+                b=torch.from_numpy(B_st).to(dev),
+                sfb=torch.from_numpy(np.ascontiguousarray(p.SB[0])).to(dev),
+                d=torch.empty((p.M, p.N), dtype=torch.bfloat16, device=dev), extra=form, ws=ws))
+            continue
         a = torch.from_numpy(p.A).to(dev)
         sfa = fp8bs.sfa_mn_major(torch.from_numpy(p.SA)).to(dev)
         b = torch.from_numpy(np.ascontiguousarray(p.B if p.kind != "dense" else p.B[0])).to(dev)
@@ -140,7 +168,13 @@ def main():
 
     def launch(q):
         p = q["p"]
-        if p.kind == "dense":
+        if p.kind == "k_grouped":
+            fp8bs.fp8bs_k_grouped_tn_contiguous(q["a"], q["sfa"], q["b"], q["sfb"], q["d"],
+                                                q["extra"], workspace=q["ws"])
+        elif isinstance(q["extra"], str):
+            getattr(fp8bs, "fp8bs_dense_" + q["extra"])(q["a"], q["sfa"], q["b"], q["sfb"], q["d"],
+                                                        workspace=q["ws"])
+        elif p.kind == "dense":
             fp8bs.fp8bs_dense_nt_ws(q["a"], q["sfa"], q["b"], q["sfb"], q["d"], workspace=q["ws"])
         elif p.kind == "contiguous":
             fp8bs.fp8bs_grouped_contiguous_nt_ws(q["a"], q["sfa"], q["b"], q["sfb"], q["d"],
@@ -246,12 +280,18 @@ def main():
         t_mfma = p.flops() / (PEAK_FP8_TFLOPS * 1e12)
         t_hbm = p.algorithmic_bytes() / (PEAK_HBM_GBS * 1e9)
         bound = "mfma" if t_mfma >= t_hbm else "hbm"
-        plan = fp8bs.describe_config({"dense": 0, "contiguous": 1, "masked": 2}[p.kind],
-                                     p.max_m if p.kind == "masked" else p.M, p.N, p.K, p.G,
-                                     p.expected_m)
+        if p.kind == "k_grouped":
+            plan = fp8bs.describe_config(fp8bs.LAYOUT_K_GROUPED, p.M, p.N, p.K, p.G, 0)
+        elif isinstance(q["extra"], str):
+            plan = fp8bs.describe_config({"nn": fp8bs.LAYOUT_DENSE_NN, "tn": fp8bs.LAYOUT_DENSE_TN,
+                                          "tt": fp8bs.LAYOUT_DENSE_TT}[q["extra"]], p.M, p.N, p.K)
+        else:
+            plan = fp8bs.describe_config({"dense": 0, "contiguous": 1, "masked": 2}[p.kind],
+                                         p.max_m if p.kind == "masked" else p.M, p.N, p.K, p.G,
+                                         p.expected_m)
         per_shape.append(dict(
             name=q["desc"]["name"], kind=p.kind, M=p.M, N=p.N, K=p.K, G=p.G,
-            valid_rows=p.valid_rows, gflop=p.flops() / 1e9, mbytes=p.algorithmic_bytes() / 1e6,
+            valid_rows=p.M if p.kind == "k_grouped" else p.valid_rows, gflop=p.flops() / 1e9, mbytes=p.algorithmic_bytes() / 1e6,
             avg_us=avg_ms * 1e3, median_us=med_ms * 1e3, p10_us=times[len(times) // 10] * 1e3,
             p90_us=times[(9 * len(times)) // 10] * 1e3, tflops=tflops, gbs=gbs, bound=bound,
             roofline_frac=max(t_mfma, t_hbm) / (avg_ms * 1e-3), plan=plan))
@@ -384,8 +424,22 @@ def cpu_baseline(problems, rows_per_shape: int):
 
     flop = 0.0
     t = 0.0
+    sample = f"first {rows_per_shape} valid rows of D (all columns) of each shape in the step"
     for q in problems:
         p = q["p"]
+        if p.kind == "k_grouped":
+            # the first R features of A (all N columns, every group): the oracle on that
+            # slice of the operands
+            R = max(1, rows_per_shape // 64)
+            sample = (f"the first {R} rows (all columns, every group) of each K-grouped "
+                      f"shape's D")
+            A_s = np.ascontiguousarray(p.A[:, :R])
+            SA_s = np.ascontiguousarray(p.SA[:R])
+            t0 = time.perf_counter()
+            oracle.k_grouped(A_s, SA_s, p.B, p.SB, p.ks)
+            t += time.perf_counter() - t0
+            flop += 2.0 * R * p.N * p.K
+            continue
         valid = np.nonzero(_valid_rows(p))[0][:rows_per_shape]
         rows = np.repeat(valid, p.N)
         cols = np.tile(np.arange(p.N), valid.size)
@@ -398,8 +452,7 @@ def cpu_baseline(problems, rows_per_shape: int):
         flop += 2.0 * rows.size * p.K
     return {"value": flop / t / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
             "kind": "oracle", "seconds": round(t, 3),
-            "sample": f"first {rows_per_shape} valid rows of D (all columns) of each shape in "
-                      f"the step, {flop / 1e9:.1f} GFLOP"}
+            "sample": f"{sample}, {flop / 1e9:.1f} GFLOP"}
 
 
 def _valid_rows(p):

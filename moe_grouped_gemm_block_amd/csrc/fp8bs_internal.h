@@ -48,7 +48,8 @@ struct InstanceShape {
     int stream_chunk_ns; // the same two when the operands stream from HBM (few rows)
     int stream_tile_ns;
     int ue8m0;           // 1: also compiled for packed UE8M0 scales
-    int mn;              // 1: also compiled for MN-major operands (nn / tn / tt, K-grouped)
+    int mn;              // > 0: also compiled for MN-major operands (nn / tn / tt, K-grouped);
+                         // the K-grouped layout's cost in percent of the model
 };
 
 // LDS bytes of one pipeline stage: the A tile, the B tile (128 K bytes per

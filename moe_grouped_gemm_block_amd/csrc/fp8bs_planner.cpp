@@ -171,6 +171,7 @@ double estimate(const Request& r, const InstanceShape& s, int splits) {
     // down unevenly as they miss in L2); measured, they lose to the B-streaming kernel
     // unless the model favours them by a wide margin.
     if (streaming && s.kind == kStaged) t *= kStagedStreamingBias;
+    if (kg) t *= s.mn / 100.0;                   // measured K-grouped cost of the instance
     const double d_bytes = (double)r.G * r.eff_rows * r.n * (kg ? 4 : 2);
     double bytes = kg ? (double)r.k * (r.m + r.n) + d_bytes
                       : (double)r.G * r.eff_rows * r.k + (double)r.G * r.n * r.k + d_bytes;
@@ -285,7 +286,7 @@ void export_plan(const Plan& p, fp8bs_plan* out) {
     out->workspace_bytes = p.workspace_bytes;
     out->kind = p.shape.kind;
     out->ue8m0 = p.shape.ue8m0;
-    out->mn = p.shape.mn;
+    out->mn = p.shape.mn != 0;
 }
 
 }  // namespace fp8bs

@@ -311,7 +311,9 @@ KGROUPED_MN = [(4096, 7168), (7168, 2048)]
 
 
 def workload_shapes(family: int) -> List[dict]:
-    """Shape descriptors (no data) for workload family 0..4."""
+    """Shape descriptors (no data) for workload family 0..6 (5: K-grouped weight
+    gradients; 6: the dense nn / tn / tt stored forms, "form" naming how A and B are
+    stored)."""
     out = []
     if family == 0:
         out.append(dict(kind="dense", M=128, N=2112, K=7168, seed=0, name="dense_m128_n2112_k7168"))
@@ -334,6 +336,10 @@ def workload_shapes(family: int) -> List[dict]:
         for j, (n, k) in enumerate(MOE_NK):
             out.append(dict(kind="masked", G=16, max_m=256, N=n, K=k, expected_m=128,
                             seed=4000 + j, name=f"masked_g16_m256_n{n}_k{k}"))
+    elif family == 6:
+        for j, form in enumerate(("nn", "tn", "tt")):
+            out.append(dict(kind="dense", M=4096, N=4096, K=7168, seed=6000 + j, form=form,
+                            name=f"dense_{form}_m4096_n4096_k7168"))
     elif family == 5:
         for j, (m, n) in enumerate(KGROUPED_MN):
             out.append(dict(kind="k_grouped", G=8, M=m, N=n, seed=5000 + j,
