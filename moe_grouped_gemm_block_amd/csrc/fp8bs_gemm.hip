@@ -218,6 +218,21 @@ __device__ __forceinline__ bool next_unit(const GemmParams& p, int u, Unit& w,
     return false;
 }
 
+// 4x4 transpose of one register across the four 16-lane rows of a wavefront: on entry
+// x[r] of row q is element (q, r); on exit x[r] of row q is element (r, q).
+// v_permlane32_swap exchanges rows 2-3 of its first operand with rows 0-1 of its second,
+// v_permlane16_swap the odd rows of the first with the even rows of the second.
+__device__ __forceinline__ void transpose_quarters(uint32_t (&x)[4]) {
+    auto a = __builtin_amdgcn_permlane32_swap(x[0], x[2], false, false);
+    auto b = __builtin_amdgcn_permlane32_swap(x[1], x[3], false, false);
+    auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+    auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+    x[0] = c[0];
+    x[1] = c[1];
+    x[2] = d[0];
+    x[3] = d[1];
+}
+
 // Rows / columns this lane holds in a tile and the store of an accumulator set:
 // lane (j = l%16, quarter kq = l/16) of wavefront (wm, wn) owns rows
 // m0 + wm*WTM + TM*j + (i ^ flip) (ROWS16: m0 + wm*WTM + 16*i + j, the row order of an
@@ -255,36 +270,69 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const Tile& tl, 
     const int64_t slot = LAYOUT == kMasked ? (int64_t)tl.g * p.m * p.n : (int64_t)0;
     uint16_t* d_g = p.d + slot;
     const bool vec_ok = (p.n & 3) == 0;
+    const bool wide_ok = (p.n & 7) == 0;              // rows start 16-byte aligned
+    constexpr int NG = TN / 4;                        // groups of four column blocks
+    // this lane's four results of block j, plus C, as two BF16 pairs
+    auto packed = [&](int i, int j, const float* crow, uint32_t& lo, uint32_t& hi) {
+        const int col = tl.n0 + wn * WTN + 16 * j + 4 * kq;
+        f32x4 v = acc[i][j];
+        if (crow) {                                  // D = C + A B^T
+            if (vec_ok && col + 3 < p.n) {
+                v += *(const f32x4*)(crow + col);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (col + e < p.n) v[e] += crow[col + e];
+            }
+        }
+        lo = pack_bf16x2(v[0], v[1]);
+        hi = pack_bf16x2(v[2], v[3]);
+    };
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
         const int row = tl.m0 + wm * WTM + (ROWS16 ? 16 * i + lj : TM * lj + (i ^ flip));
         bool ok = row < tl.row_limit;
         if (LAYOUT == kContiguous && ok) ok = p.grouped_layout[row] == tl.g;
-        if (!ok) continue;
         uint16_t* drow = d_g + (int64_t)row * p.n;
-        const float* crow = p.c ? p.c + slot + (int64_t)row * p.n : nullptr;
+        const float* crow = (p.c && ok) ? p.c + slot + (int64_t)row * p.n : nullptr;
+        // Four column blocks at a time: the four lanes of a row (quarters kq = 0..3) hold
+        // columns 4kq..4kq+3 of every block; a 4x4 exchange across quarters (two rounds of
+        // gfx950 row swaps) leaves quarter kq with all 16 columns of block 4g + kq, stored
+        // as two 16-byte writes, so a row's 4 blocks go out as one 128-byte run.  Every
+        // lane takes part in the exchange; rows that are not written skip the stores.
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int col = tl.n0 + wn * WTN + 16 * j + 4 * kq;
-            f32x4 v = acc[i][j];
-            if (crow) {                                  // D = C + A B^T
-                if (vec_ok && col + 3 < p.n) {
-                    v += *(const f32x4*)(crow + col);
-                } else {
+        for (int g = 0; g < NG; ++g) {
+            uint32_t lo[4], hi[4];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (col + e < p.n) v[e] += crow[col + e];
-                }
-            }
-            if (vec_ok && col + 3 < p.n) {
-                uint2 w;
-                w.x = pack_bf16x2(v[0], v[1]);
-                w.y = pack_bf16x2(v[2], v[3]);
-                *(uint2*)(drow + col) = w;
+            for (int jj = 0; jj < 4; ++jj) packed(i, 4 * g + jj, crow, lo[jj], hi[jj]);
+            transpose_quarters(lo);
+            transpose_quarters(hi);
+            if (!ok) continue;
+            const int cb = tl.n0 + wn * WTN + 16 * (4 * g + kq);
+            if (wide_ok && cb + 15 < p.n) {
+                *(uint4*)(drow + cb) = uint4{lo[0], hi[0], lo[1], hi[1]};
+                *(uint4*)(drow + cb + 8) = uint4{lo[2], hi[2], lo[3], hi[3]};
             } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (col + e < p.n) drow[col + e] = to_bf16(v[e]);
+                for (int c = 0; c < 16; ++c) {
+                    const uint32_t w = (c & 2) ? hi[c >> 2] : lo[c >> 2];
+                    if (cb + c < p.n) drow[cb + c] = (uint16_t)(w >> (16 * (c & 1)));
+                }
+            }
+        }
+        if (!ok) continue;
+#pragma unroll
+        for (int j = 4 * NG; j < TN; ++j) {
+            const int col = tl.n0 + wn * WTN + 16 * j + 4 * kq;
+            uint32_t lo, hi;
+            packed(i, j, crow, lo, hi);
+            if (vec_ok && col + 3 < p.n) {
+                *(uint2*)(drow + col) = uint2{lo, hi};
+            } else {
+                if (col < p.n) drow[col] = (uint16_t)lo;
+                if (col + 1 < p.n) drow[col + 1] = (uint16_t)(lo >> 16);
+                if (col + 2 < p.n) drow[col + 2] = (uint16_t)hi;
+                if (col + 3 < p.n) drow[col + 3] = (uint16_t)(hi >> 16);
             }
         }
     }
