@@ -221,3 +221,13 @@ def test_chunk_sum_precision_assumption():
     ratio = np.abs(gpu - exact)[largest > 0] / largest[largest > 0]
     print(f"[gpu] chunk sum: max error / largest product = 2^{np.log2(ratio.max() + 1e-300):.1f}")
     assert ratio.max() <= 2.0 ** -9
+
+
+def test_most_groups_the_call_takes():
+    """256 groups (the most one call takes), many of them empty, the rest one or two
+    chunks, with C: every group's offset in the kernel arguments is exercised."""
+    rng = np.random.default_rng(970)
+    counts = rng.integers(0, 200, size=256) * (rng.random(256) < 0.5)
+    p = synth.make_k_grouped(256, 32, 48, seed=971, counts=counts)
+    C = rng.standard_normal((256, 32, 48)).astype(np.float32)
+    _full(p, "256 groups", C=C)

@@ -107,3 +107,20 @@ def test_refusals():
     with pytest.raises(fp8bs.FP8BSError):
         _run(p, "tn")
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("desc", synth.workload_shapes(6), ids=lambda d: d["name"])
+def test_full_size_stored_forms_sampled(desc):
+    """The benchmark's stored-form shapes at full size in its launch configuration (the
+    planner's plan with its preferred workspace): every output finite, 4100 sampled
+    outputs against the oracle."""
+    from _helpers import check_sampled
+    p = synth.make(desc)
+    form = desc["form"]
+    print(f"[gpu] full size {desc['name']}", flush=True)
+    code = {"nn": fp8bs.LAYOUT_DENSE_NN, "tn": fp8bs.LAYOUT_DENSE_TN,
+            "tt": fp8bs.LAYOUT_DENSE_TT}[form]
+    ws = torch.empty(max(fp8bs.workspace_size(code, p.M, p.N, p.K), 16), dtype=torch.uint8,
+                     device="cuda")
+    gpu = _run(p, form, workspace=ws)
+    check_sampled(p, gpu, n_points=4096, seed=p.seed, what=desc["name"])
