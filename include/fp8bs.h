@@ -278,6 +278,34 @@ int fp8bs_k_grouped_tn_contiguous(const void* a, const float* sfa, const void* b
                                   int num_groups, int m, int n, int k_total, void* workspace,
                                   size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Power-of-two scale variants of the stored-form and K-grouped calls (the SM100 form of
+ * the pages: packed UE8M0, [hada] "Giao diện GEMM và ràng buộc layout").  Scales are
+ * packed four K groups per int32 exactly as for fp8bs_dense_nt_ue8m0:
+ *   dense nn / tn / tt: sfa int32 [ceil(k/512)][fp8bs_get_sfa_ld(m)] (MN-major),
+ *                       sfb int32 [ceil(n/128)][ceil(k/512)];
+ *   K-grouped:          sfa int32 [ceil(k_total/512)][fp8bs_get_sfa_ld(m)],
+ *                       sfb int32 [ceil(k_total/512)][fp8bs_get_sfa_ld(n)]
+ *                       (one exponent per feature and 128-token chunk on both sides).
+ * Everything else (operands, C, D, ks, workspace, preconditions, errors) is as for the
+ * FP32-scale calls above; the matrix core applies both exponents and accumulates across
+ * chunks, so the result has the promotion-free rounding of the UE8M0 NT calls.
+ */
+int fp8bs_dense_nn_ue8m0(const void* a, const int32_t* sfa, const void* b, const int32_t* sfb,
+                         const float* c, void* d, int m, int n, int k, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+int fp8bs_dense_tn_ue8m0(const void* a, const int32_t* sfa, const void* b, const int32_t* sfb,
+                         const float* c, void* d, int m, int n, int k, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+int fp8bs_dense_tt_ue8m0(const void* a, const int32_t* sfa, const void* b, const int32_t* sfb,
+                         const float* c, void* d, int m, int n, int k, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+int fp8bs_k_grouped_tn_contiguous_ue8m0(const void* a, const int32_t* sfa, const void* b,
+                                        const int32_t* sfb, const float* c, float* d,
+                                        const int32_t* ks, int num_groups, int m, int n,
+                                        int k_total, void* workspace, size_t workspace_bytes,
+                                        hipStream_t stream);
+
 /* Workspace bytes the planner's preferred plan uses for a request on the current
  * device (CU cap respected; `m` as in fp8bs_plan_query).  0 means the best plan
  * splits nothing.  Passing at least this much to a _ws call lets it use that

@@ -32,6 +32,8 @@ __all__ = [
     "ue8m0_exponents", "pack_ue8m0", "sfa_ue8m0_mn_major", "sfb_ue8m0",
     "fp8bs_dense_nt_c", "fp8bs_grouped_contiguous_nt_c", "fp8bs_grouped_masked_nt_c",
     "fp8bs_dense_nn", "fp8bs_dense_tn", "fp8bs_dense_tt", "fp8bs_k_grouped_tn_contiguous",
+    "fp8bs_dense_nn_ue8m0", "fp8bs_dense_tn_ue8m0", "fp8bs_dense_tt_ue8m0",
+    "fp8bs_k_grouped_tn_contiguous_ue8m0",
     "LAYOUT_DENSE", "LAYOUT_CONTIGUOUS", "LAYOUT_MASKED", "LAYOUT_K_GROUPED",
     "LAYOUT_DENSE_NN", "LAYOUT_DENSE_TN", "LAYOUT_DENSE_TT",
 ]
@@ -110,6 +112,9 @@ def _load():
     for f in ("nn", "tn", "tt"):
         getattr(lib, "fp8bs_dense_" + f).argtypes = [P, P, P, P, P, P, I, I, I, P, S, P]
     lib.fp8bs_k_grouped_tn_contiguous.argtypes = [P, P, P, P, P, P, P, I, I, I, I, P, S, P]
+    for f in ("nn", "tn", "tt"):
+        getattr(lib, "fp8bs_dense_" + f + "_ue8m0").argtypes = [P, P, P, P, P, P, I, I, I, P, S, P]
+    lib.fp8bs_k_grouped_tn_contiguous_ue8m0.argtypes = [P, P, P, P, P, P, P, I, I, I, I, P, S, P]
     lib.fp8bs_describe_config.argtypes = [I, I64, I, I, I, I, ctypes.c_char_p, ctypes.c_size_t]
     lib.fp8bs_count_tiles.argtypes = [I, I64, I, I, I, I]
     lib.fp8bs_count_tiles.restype = I64
@@ -650,7 +655,7 @@ def fp8bs_grouped_masked_nt_c(a, sfa, b, sfb, c, d, masked_m, expected_m: int = 
 
 # ---- stored forms nn / tn / tt and the K-grouped (weight-gradient) GEMM --------
 
-def _dense_form(form, a, sfa, b, sfb, c, d, workspace, stream):
+def _dense_form(form, a, sfa, b, sfb, c, d, workspace, stream, e8=False):
     torch = _torch()
     a_t, b_t = form[0] == "t", form[1] == "t"
     if a.dim() != 2 or b.dim() != 2:
@@ -660,19 +665,24 @@ def _dense_form(form, a, sfa, b, sfb, c, d, workspace, stream):
     if kb_ != k or tuple(d.shape) != (m, n):
         raise ValueError("shape mismatch between a, b and d")
     kb = k // 128 if k % 128 == 0 else -1
-    args = (_dev_ptr(a, "a", _fp8_dtypes(), 2), _dev_ptr(sfa, "sfa", (torch.float32,)),
-            _dev_ptr(b, "b", _fp8_dtypes(), 2), _dev_ptr(sfb, "sfb", (torch.float32,)))
-    if kb > 0 and (sfa.numel() != kb * get_sfa_ld(m) or sfb.numel() != ((n + 127) // 128) * kb):
-        raise ValueError("scale tensor sizes do not match the shapes")
+    if e8:
+        sap, sbp = _ue8m0_checks(sfa, sfb, 1, 1, m, n, k)
+    else:
+        sap = _dev_ptr(sfa, "sfa", (torch.float32,))
+        sbp = _dev_ptr(sfb, "sfb", (torch.float32,))
+        if kb > 0 and (sfa.numel() != kb * get_sfa_ld(m) or
+                       sfb.numel() != ((n + 127) // 128) * kb):
+            raise ValueError("scale tensor sizes do not match the shapes")
+    args = (_dev_ptr(a, "a", _fp8_dtypes(), 2), sap, _dev_ptr(b, "b", _fp8_dtypes(), 2), sbp)
     dp = _dev_ptr(d, "d", _bf16_dtypes(), 2)
     cp = _addend(c, d) if c is not None else ctypes.c_void_p(None)
     code = {"nn": LAYOUT_DENSE_NN, "tn": LAYOUT_DENSE_TN, "tt": LAYOUT_DENSE_TT}[form]
+    name = "fp8bs_dense_" + form + ("_ue8m0" if e8 else "")
     with torch.cuda.device(a.device):
         s = _stream(stream, a.device)
         wp, wb, _keep = _workspace(workspace, code, m, n, k, 1, 0, s, a.device)
-        st = getattr(_load(), "fp8bs_dense_" + form)(*args, cp, dp, m, n, k, wp, wb,
-                                                     ctypes.c_void_p(s.cuda_stream))
-    _check(st, "fp8bs_dense_" + form)
+        st = getattr(_load(), name)(*args, cp, dp, m, n, k, wp, wb, ctypes.c_void_p(s.cuda_stream))
+    _check(st, name)
 
 
 def fp8bs_dense_nn(a, sfa, b, sfb, d, c=None, workspace=None, stream=None):
@@ -691,6 +701,30 @@ def fp8bs_dense_tt(a, sfa, b, sfb, d, c=None, workspace=None, stream=None):
     _dense_form("tt", a, sfa, b, sfb, c, d, workspace, stream)
 
 
+def fp8bs_dense_nn_ue8m0(a, sfa, b, sfb, d, c=None, workspace=None, stream=None):
+    """fp8bs_dense_nn with packed UE8M0 scales (sfa int32 [ceil(k/512)][ld(m)], sfb int32
+    [ceil(n/128)][ceil(k/512)])."""
+    _dense_form("nn", a, sfa, b, sfb, c, d, workspace, stream, e8=True)
+
+
+def fp8bs_dense_tn_ue8m0(a, sfa, b, sfb, d, c=None, workspace=None, stream=None):
+    """fp8bs_dense_tn with packed UE8M0 scales."""
+    _dense_form("tn", a, sfa, b, sfb, c, d, workspace, stream, e8=True)
+
+
+def fp8bs_dense_tt_ue8m0(a, sfa, b, sfb, d, c=None, workspace=None, stream=None):
+    """fp8bs_dense_tt with packed UE8M0 scales."""
+    _dense_form("tt", a, sfa, b, sfb, c, d, workspace, stream, e8=True)
+
+
+def fp8bs_k_grouped_tn_contiguous_ue8m0(a, sfa, b, sfb, d, ks, c=None, workspace=None,
+                                        stream=None):
+    """K-grouped GEMM with packed UE8M0 scales: sfa int32 [ceil(k_total/512)][ld(m)], sfb
+    int32 [ceil(k_total/512)][ld(n)] (``sfa_ue8m0_mn_major`` of the logical [m][k/128] /
+    [n][k/128] power-of-two scales)."""
+    _k_grouped(a, sfa, b, sfb, d, ks, c, workspace, stream, e8=True)
+
+
 def fp8bs_k_grouped_tn_contiguous(a, sfa, b, sfb, d, ks, c=None, workspace=None, stream=None):
     """K-grouped weight-gradient GEMM: D[g] = C[g] + A_g^T B_g in FP32.
 
@@ -698,6 +732,10 @@ def fp8bs_k_grouped_tn_contiguous(a, sfa, b, sfb, d, ks, c=None, workspace=None,
     sfb: f32 [k_total/128][ld(n)]; d: f32 [g][m][n] (every element written); ks: the g
     group sizes along K (a host sequence of ints, multiples of 128 adding up to k_total);
     c: optional f32 [g][m][n] (may be d itself)."""
+    _k_grouped(a, sfa, b, sfb, d, ks, c, workspace, stream, e8=False)
+
+
+def _k_grouped(a, sfa, b, sfb, d, ks, c, workspace, stream, e8):
     torch = _torch()
     sizes = [int(x) for x in ks]
     g = len(sizes)
@@ -708,9 +746,11 @@ def fp8bs_k_grouped_tn_contiguous(a, sfa, b, sfb, d, ks, c=None, workspace=None,
     if b.shape[0] != k_total or tuple(d.shape) != (g, m, n):
         raise ValueError("shape mismatch between a, b, d and ks")
     kb = k_total // 128 if k_total % 128 == 0 else -1
-    args = (_dev_ptr(a, "a", _fp8_dtypes(), 2), _dev_ptr(sfa, "sfa", (torch.float32,)),
-            _dev_ptr(b, "b", _fp8_dtypes(), 2), _dev_ptr(sfb, "sfb", (torch.float32,)))
-    if kb >= 0 and (sfa.numel() != kb * get_sfa_ld(m) or sfb.numel() != kb * get_sfa_ld(n)):
+    rows = (kb + 3) // 4 if e8 else kb                  # packed words: four chunks per int32
+    sdt = torch.int32 if e8 else torch.float32
+    args = (_dev_ptr(a, "a", _fp8_dtypes(), 2), _dev_ptr(sfa, "sfa", (sdt,)),
+            _dev_ptr(b, "b", _fp8_dtypes(), 2), _dev_ptr(sfb, "sfb", (sdt,)))
+    if kb >= 0 and (sfa.numel() != rows * get_sfa_ld(m) or sfb.numel() != rows * get_sfa_ld(n)):
         raise ValueError("scale tensor sizes do not match the shapes")
     dp = _dev_ptr(d, "d", (torch.float32,), 3)
     cp = _addend(c, d) if c is not None else ctypes.c_void_p(None)
@@ -718,6 +758,7 @@ def fp8bs_k_grouped_tn_contiguous(a, sfa, b, sfb, d, ks, c=None, workspace=None,
     with torch.cuda.device(a.device):
         s = _stream(stream, a.device)
         wp, wb, _keep = _workspace(workspace, LAYOUT_K_GROUPED, m, n, k_total, g, 0, s, a.device)
-        st = _load().fp8bs_k_grouped_tn_contiguous(*args, cp, dp, ks_host, g, m, n, k_total,
-                                                   wp, wb, ctypes.c_void_p(s.cuda_stream))
-    _check(st, "fp8bs_k_grouped_tn_contiguous")
+        name = "fp8bs_k_grouped_tn_contiguous" + ("_ue8m0" if e8 else "")
+        st = getattr(_load(), name)(*args, cp, dp, ks_host, g, m, n, k_total, wp, wb,
+                                    ctypes.c_void_p(s.cuda_stream))
+    _check(st, name)

@@ -284,6 +284,40 @@ int fp8bs_k_grouped_tn_contiguous(const void* a, const float* sfa, const void* b
                workspace ? workspace_bytes : 0, stream, fp8bs::kScaleF32, c, c != nullptr);
 }
 
+int fp8bs_dense_nn_ue8m0(const void* a, const int32_t* sfa, const void* b, const int32_t* sfb,
+                         const float* c, void* d, int m, int n, int k, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+    return run(fp8bs::kDense, a, (const float*)sfa, b, (const float*)sfb, d, nullptr, m, n, k, 1, 0,
+               workspace, workspace ? workspace_bytes : 0, stream, fp8bs::kScaleUE8M0, c,
+               c != nullptr, fp8bs::kFormNN);
+}
+
+int fp8bs_dense_tn_ue8m0(const void* a, const int32_t* sfa, const void* b, const int32_t* sfb,
+                         const float* c, void* d, int m, int n, int k, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+    return run(fp8bs::kDense, a, (const float*)sfa, b, (const float*)sfb, d, nullptr, m, n, k, 1, 0,
+               workspace, workspace ? workspace_bytes : 0, stream, fp8bs::kScaleUE8M0, c,
+               c != nullptr, fp8bs::kFormTN);
+}
+
+int fp8bs_dense_tt_ue8m0(const void* a, const int32_t* sfa, const void* b, const int32_t* sfb,
+                         const float* c, void* d, int m, int n, int k, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+    return run(fp8bs::kDense, a, (const float*)sfa, b, (const float*)sfb, d, nullptr, m, n, k, 1, 0,
+               workspace, workspace ? workspace_bytes : 0, stream, fp8bs::kScaleUE8M0, c,
+               c != nullptr, fp8bs::kFormTT);
+}
+
+int fp8bs_k_grouped_tn_contiguous_ue8m0(const void* a, const int32_t* sfa, const void* b,
+                                        const int32_t* sfb, const float* c, float* d,
+                                        const int32_t* ks, int num_groups, int m, int n,
+                                        int k_total, void* workspace, size_t workspace_bytes,
+                                        hipStream_t stream) {
+    return run(fp8bs::kKGrouped, a, (const float*)sfa, b, (const float*)sfb, d, ks, m, n, k_total,
+               num_groups, 0, workspace, workspace ? workspace_bytes : 0, stream,
+               fp8bs::kScaleUE8M0, c, c != nullptr);
+}
+
 int64_t fp8bs_workspace_size(int layout_code, int64_t m, int n, int k, int num_groups,
                              int expected_m) {
     int layout, form;

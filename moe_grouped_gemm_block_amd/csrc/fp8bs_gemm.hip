@@ -358,12 +358,12 @@ __global__ void __launch_bounds__(64 * WM * WN) fp8bs_gemm_kernel(GemmParams p) 
     // fragments are read with transpose loads; an MN-major A's 16-row blocks are 16
     // consecutive rows (ROWS16 in store_tile).
     // LAYOUT == kKGrouped: both operands MN-major, per-group K ranges, B scaled per column
-    // (SFB [K_total/128][sfb_ld]), FP32 output.
+    // (SFB [K_total/128][sfb_ld], or packed words [ceil(K_total/512)][sfb_ld]), FP32 output.
     constexpr bool E8 = SCALE == kScaleUE8M0;
     constexpr bool KG = LAYOUT == kKGrouped;
     static_assert(!KG || (AMN && BMN), "the K-grouped layout has MN-major operands");
-    static_assert(!(AMN || BMN) || (SCALE == kScaleF32 && (LAYOUT == kDense || KG)),
-                  "MN-major operands: dense or K-grouped, FP32 scales");
+    static_assert(!(AMN || BMN) || LAYOUT == kDense || KG,
+                  "MN-major operands: dense or K-grouped");
     constexpr int NW = WM * WN;                      // wavefronts per workgroup
     constexpr int WTM = BM / WM, WTN = BN / WN;      // wavefront sub-tile
     constexpr int TM = WTM / 16, TN = WTN / 16;      // 16x16 blocks per wavefront
@@ -540,7 +540,7 @@ __global__ void __launch_bounds__(64 * WM * WN) fp8bs_gemm_kernel(GemmParams p) 
             // the tile's block_n per-column B scales of chunk c (MN-major SFB, contiguous);
             // wavefront NW-2 copies them, the others repeat its first 16 bytes so that
             // every wavefront issues one copy per chunk
-            const uint8_t* sb_row = (const uint8_t*)(p.sfb + (int64_t)c * p.sfb_ld);
+            const uint8_t* sb_row = (const uint8_t*)(p.sfb + (int64_t)(E8 ? c / 4 : c) * p.sfb_ld);
             int c4 = tl.n0 + 4 * lane;                // columns past the scale row are unused
             if (c4 >= p.sfb_ld) c4 = 0;
             const bool mine = wave == NW - 2 ? 4 * lane < BN : lane == 0;
@@ -599,6 +599,7 @@ __global__ void __launch_bounds__(64 * WM * WN) fp8bs_gemm_kernel(GemmParams p) 
         float sa[TM];
         float sb[UNIFORM_SB ? 1 : TN];
         f32x4 sbv[KG ? TN : 1];                       // K-grouped: the lane's four columns
+        int sbw[KG && E8 ? TN : 1];                   // K-grouped UE8M0: the lane's B row's word
     };
     auto load_scales = [&](const uint8_t* st, const Tile& tl, ScaleRegs& r) {
         const float* sap = (const float*)(st + sa_rd);
@@ -609,7 +610,14 @@ __global__ void __launch_bounds__(64 * WM * WN) fp8bs_gemm_kernel(GemmParams p) 
 #pragma unroll
             for (int i = 0; i < TM; ++i) r.sa[i] = sap[i];
         }
-        if constexpr (KG) {
+        if constexpr (KG && E8) {
+            // the exponent word of the B row this lane feeds to the matrix core (column
+            // wn*WTN + 16j + lj), not of its output columns
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                r.sbw[j] = *(const int*)(st + SB_OFF + (wn * WTN + 16 * j + lj) * 4);
+            return;
+        } else if constexpr (KG) {
 #pragma unroll
             for (int j = 0; j < TN; ++j)
                 r.sbv[j] = *(const f32x4*)(st + SB_OFF + (wn * WTN + 16 * j + 4 * kq) * 4);
@@ -705,13 +713,22 @@ __global__ void __launch_bounds__(64 * WM * WN) fp8bs_gemm_kernel(GemmParams p) 
 
         const uint8_t* st = smem + sq * STAGE;
         float sc[TM][UNIFORM_SB ? 1 : TN];
-        int sae[E8 ? TM : 1], sbe[E8 ? (UNIFORM_SB ? 1 : TN) : 1];   // E8M0 exponents
+        // E8M0 exponents; a B exponent per column block unless one serves the whole
+        // wavefront (K-grouped: one per lane and block)
+        constexpr bool SB_PER_J = KG || !UNIFORM_SB;
+        int sae[E8 ? TM : 1], sbe[E8 ? (SB_PER_J ? TN : 1) : 1];
         float kg_sa[KG ? TM : 1];
         f32x4 kg_sb[KG ? TN : 1];
         {
             ScaleRegs sr;
             load_scales(st, cur.tl, sr);
-            if constexpr (KG) {
+            if constexpr (KG && E8) {
+                const int sh = 8 * (c & 3);
+#pragma unroll
+                for (int i = 0; i < TM; ++i) sae[i] = (__builtin_bit_cast(int, sr.sa[i]) >> sh) & 0xFF;
+#pragma unroll
+                for (int j = 0; j < TN; ++j) sbe[j] = (sr.sbw[j] >> sh) & 0xFF;
+            } else if constexpr (KG) {
 #pragma unroll
                 for (int i = 0; i < TM; ++i) kg_sa[i] = sr.sa[i];
 #pragma unroll
@@ -732,7 +749,7 @@ __global__ void __launch_bounds__(64 * WM * WN) fp8bs_gemm_kernel(GemmParams p) 
         }
         auto promote = [&](int o, int q, const f32x4& part) {
             const int i = STREAM_A ? o : q, j = STREAM_A ? q : o;
-            if constexpr (KG)
+            if constexpr (KG && !E8)
                 acc[i][j] += (part * kg_sa[i]) * kg_sb[j];  // row scale, then per column
             else
                 acc[i][j] += part * sc[i][UNIFORM_SB ? 0 : j];
@@ -750,7 +767,7 @@ __global__ void __launch_bounds__(64 * WM * WN) fp8bs_gemm_kernel(GemmParams p) 
                 // first operand B rows (scale: their 128x128 block), second A rows (row scale)
                 acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                     STREAM_A ? res[q] : fr, STREAM_A ? fr : res[q], acc[i][j], 0, 0,
-                    0, sbe[UNIFORM_SB ? 0 : j], 0, sae[i]);
+                    0, sbe[SB_PER_J ? j : 0], 0, sae[i]);
                 __builtin_amdgcn_s_setprio(0);
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             } else {
@@ -1131,6 +1148,8 @@ struct InstanceEntry {
     KernelFn fn_kg;            // K-grouped
     KernelFn reduce_amn;       // dense with an MN-major A (tn, tt)
     KernelFn reduce_kg;
+    KernelFn fn_form_e8[4];    // the same with packed UE8M0 scales (null: not compiled)
+    KernelFn fn_kg_e8;
 };
 
 template <int KIND, int BM, int BN, int WM, int WN, int NS, int LAYOUT, int SCALE>
@@ -1153,18 +1172,20 @@ constexpr KernelFn e8_fn() {
 // MN-major variants (staged kernel only): LAYOUT kDense with the form's operand majors, or
 // kKGrouped; REDUCE picks the matching split-K reduction instead.
 template <int KIND, int BM, int BN, int WM, int WN, int NS, int MN, int LAYOUT, bool AMN,
-          bool BMN, bool REDUCE = false>
+          bool BMN, bool REDUCE = false, int E8 = -1>
 constexpr KernelFn mn_fn() {
-    if constexpr (!MN || KIND != kStaged) {
+    // E8 < 0: FP32 scales; 0 / 1: the instance's UE8M0 flag (packed power-of-two scales)
+    if constexpr (!MN || KIND != kStaged || E8 == 0) {
         return nullptr;
     } else if constexpr (REDUCE) {
         return fp8bs_splitk_reduce<BM, BN, WM, WN, LAYOUT, AMN>;
     } else {
-        return fp8bs_gemm_kernel<BM, BN, WM, WN, NS, LAYOUT, kScaleF32, AMN, BMN>;
+        return fp8bs_gemm_kernel<BM, BN, WM, WN, NS, LAYOUT, (E8 > 0 ? kScaleUE8M0 : kScaleF32),
+                                 AMN, BMN>;
     }
 }
 
-#define FP8BS_INSTANCE(KIND, BM, BN, WM, WN, NS, OCC, CNS, TNS, SCNS, STNS, E8, MN)        \
+#define FP8BS_INSTANCE(KIND, BM, BN, WM, WN, NS, OCC, CNS, TNS, SCNS, STNS, E8, MN, MNE8)  \
     {{gemm_fn<KIND, BM, BN, WM, WN, NS, kDense, kScaleF32>(),                              \
       gemm_fn<KIND, BM, BN, WM, WN, NS, kContiguous, kScaleF32>(),                         \
       gemm_fn<KIND, BM, BN, WM, WN, NS, kMasked, kScaleF32>()},                            \
@@ -1181,7 +1202,12 @@ constexpr KernelFn mn_fn() {
       mn_fn<KIND, BM, BN, WM, WN, NS, MN, kDense, true, false>()},                          \
      mn_fn<KIND, BM, BN, WM, WN, NS, MN, kKGrouped, true, true>(),                          \
      mn_fn<KIND, BM, BN, WM, WN, NS, MN, kDense, true, false, true>(),                      \
-     mn_fn<KIND, BM, BN, WM, WN, NS, MN, kKGrouped, true, true, true>()},
+     mn_fn<KIND, BM, BN, WM, WN, NS, MN, kKGrouped, true, true, true>(),                    \
+     {nullptr,                                                                              \
+      mn_fn<KIND, BM, BN, WM, WN, NS, MN, kDense, false, true, false, E8>(),                \
+      mn_fn<KIND, BM, BN, WM, WN, NS, MN, kDense, true, true, false, E8>(),                 \
+      mn_fn<KIND, BM, BN, WM, WN, NS, MN, kDense, true, false, false, E8>()},               \
+     mn_fn<KIND, BM, BN, WM, WN, NS, MN, kKGrouped, true, true, false, E8>()},
 const InstanceEntry kEntries[] = {
 #include "fp8bs_instances.inc"
 };
@@ -1197,11 +1223,12 @@ int launch_instance(const Plan& plan, int layout, int scale_mode, const GemmPara
         return (int)hipErrorInvalidValue;
     const InstanceEntry& e = kEntries[plan.instance];
     KernelFn fn, reduce;
+    const bool e8 = scale_mode == kScaleUE8M0;
     if (layout == kKGrouped) {
-        fn = scale_mode == kScaleF32 ? e.fn_kg : nullptr;
+        fn = e8 ? e.fn_kg_e8 : e.fn_kg;
         reduce = e.reduce_kg;
     } else if (form != kFormNT) {
-        fn = (layout == kDense && scale_mode == kScaleF32) ? e.fn_form[form] : nullptr;
+        fn = layout != kDense ? nullptr : e8 ? e.fn_form_e8[form] : e.fn_form[form];
         reduce = form_a_mn(form) ? e.reduce_amn : e.reduce[kDense];
     } else {
         fn = scale_mode == kScaleUE8M0 ? e.fn_e8[layout] : e.fn[layout];

@@ -50,6 +50,7 @@ struct InstanceShape {
     int ue8m0;           // 1: also compiled for packed UE8M0 scales
     int mn;              // > 0: also compiled for MN-major operands (nn / tn / tt, K-grouped);
                          // the K-grouped layout's cost in percent of the model
+    int mn_e8;           // the same cost for the K-grouped layout with UE8M0 scales
 };
 
 // LDS bytes of one pipeline stage: the A tile, the B tile (128 K bytes per

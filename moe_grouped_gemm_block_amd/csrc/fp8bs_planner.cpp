@@ -16,8 +16,8 @@
 
 namespace fp8bs {
 
-#define FP8BS_INSTANCE(KIND, BM, BN, WM, WN, NS, OCC, CNS, TNS, SCNS, STNS, E8, MN) \
-    {KIND, BM, BN, WM, WN, NS, OCC, instance_lds_bytes(KIND, BM, BN, NS), CNS, TNS, SCNS, STNS, E8, MN},
+#define FP8BS_INSTANCE(KIND, BM, BN, WM, WN, NS, OCC, CNS, TNS, SCNS, STNS, E8, MN, MNE8) \
+    {KIND, BM, BN, WM, WN, NS, OCC, instance_lds_bytes(KIND, BM, BN, NS), CNS, TNS, SCNS, STNS, E8, MN, MNE8},
 const InstanceShape kInstances[] = {
 #include "fp8bs_instances.inc"
 };
@@ -89,6 +89,7 @@ namespace {
 struct Request {
     int layout;
     int form;
+    int scale_mode;
     int64_t m;
     int n, k, G;
     int64_t eff_rows;    // rows per group the estimate assumes
@@ -98,9 +99,10 @@ struct Request {
 };
 
 Request make_request(int layout, int64_t m, int n, int k, int num_groups, int expected_m,
-                     int num_cus, int64_t workspace_bytes, int form) {
+                     int num_cus, int64_t workspace_bytes, int form, int scale_mode) {
     Request r;
     r.layout = layout;
+    r.scale_mode = scale_mode;
     r.form = layout == kKGrouped ? kFormTN : form;
     r.m = m;
     r.n = n;
@@ -171,7 +173,8 @@ double estimate(const Request& r, const InstanceShape& s, int splits) {
     // down unevenly as they miss in L2); measured, they lose to the B-streaming kernel
     // unless the model favours them by a wide margin.
     if (streaming && s.kind == kStaged) t *= kStagedStreamingBias;
-    if (kg) t *= s.mn / 100.0;                   // measured K-grouped cost of the instance
+    if (kg)                                      // measured K-grouped cost of the instance
+        t *= (r.scale_mode == kScaleUE8M0 ? s.mn_e8 : s.mn) / 100.0;
     const double d_bytes = (double)r.G * r.eff_rows * r.n * (kg ? 4 : 2);
     double bytes = kg ? (double)r.k * (r.m + r.n) + d_bytes
                       : (double)r.G * r.eff_rows * r.k + (double)r.G * r.n * r.k + d_bytes;
@@ -214,11 +217,10 @@ int plan_instance(int instance, int splits, int layout, int64_t m, int n, int k,
                   int scale_mode, int form) {
     if (instance < 0 || instance >= kNumInstances || num_cus < 1) return FP8BS_ERR_UNSUPPORTED;
     const Request r = make_request(layout, m, n, k, num_groups, expected_m, num_cus,
-                                   workspace_bytes, form);
+                                   workspace_bytes, form, scale_mode);
     const InstanceShape& s = kInstances[instance];
     if (!instance_fits(r, s)) return FP8BS_ERR_UNSUPPORTED;
-    if (scale_mode == kScaleUE8M0 && (!s.ue8m0 || r.form != kFormNT || layout == kKGrouped))
-        return FP8BS_ERR_UNSUPPORTED;
+    if (scale_mode == kScaleUE8M0 && !s.ue8m0) return FP8BS_ERR_UNSUPPORTED;
     int best_s = -1;
     if (splits >= 1) {
         if (estimate(r, s, splits) < 0) return FP8BS_ERR_UNSUPPORTED;
@@ -243,10 +245,8 @@ int plan_request(int layout, int64_t m, int n, int k, int num_groups, int expect
     int st = validate_sizes(layout, m, n, k, layout == kDense ? 1 : num_groups, form);
     if (st != FP8BS_OK) return st;
     if (num_cus < 1) return FP8BS_ERR_UNSUPPORTED;
-    if (scale_mode == kScaleUE8M0 && (form != kFormNT || layout == kKGrouped))
-        return FP8BS_ERR_UNSUPPORTED;
     const Request r = make_request(layout, m, n, k, num_groups, expected_m, num_cus,
-                                   workspace_bytes, form);
+                                   workspace_bytes, form, scale_mode);
     double best_t = 0;
     int best = -1, best_s = 1;
     for (int i = 0; i < kNumInstances; ++i) {

@@ -259,3 +259,20 @@ def test_stored_form_and_k_grouped_entry_points_validate_before_launching():
     assert kg(f, f, f, f, None, f, None, 3, 64, 64, 384, None, 0, None) == ERR_POINTER
     assert kg(f, f, f, f, None, f, ks, 3, 40, 64, 384, None, 0, None) == ERR_SHAPE
     assert kg(f, f, f, f, None, None, ks, 3, 64, 64, 384, None, 0, None) == ERR_POINTER
+
+
+def test_ue8m0_stored_form_and_k_grouped_entry_points_validate_before_launching():
+    lib = fp8bs._load()
+    f = _Fake().ptr
+    for name in ("fp8bs_dense_nn_ue8m0", "fp8bs_dense_tn_ue8m0", "fp8bs_dense_tt_ue8m0"):
+        fn = getattr(lib, name)
+        assert fn(f, f, f, f, None, f, 64, 64, 100, None, 0, None) == ERR_SHAPE
+        assert fn(f, None, f, f, None, f, 64, 64, 128, None, 0, None) == ERR_POINTER
+        assert fn(f, f, f, f, None, f, 0, 64, 128, None, 0, None) == OK
+    kg = lib.fp8bs_k_grouped_tn_contiguous_ue8m0
+    ks = (ctypes.c_int32 * 2)(128, 64)
+    assert kg(f, f, f, f, None, f, ks, 2, 64, 64, 192, None, 0, None) == ERR_SHAPE
+    assert kg(f, f, f, f, None, f, None, 2, 64, 64, 256, None, 0, None) == ERR_POINTER
+    # UE8M0 plans exist for every form and the K-grouped layout
+    both = {i["instance"] for i in fp8bs.instances() if i["mn"] and i["ue8m0"]}
+    assert both

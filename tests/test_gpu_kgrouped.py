@@ -231,3 +231,56 @@ def test_most_groups_the_call_takes():
     p = synth.make_k_grouped(256, 32, 48, seed=971, counts=counts)
     C = rng.standard_normal((256, 32, 48)).astype(np.float32)
     _full(p, "256 groups", C=C)
+
+
+E8_MN_INSTANCES = [i["instance"] for i in fp8bs.instances() if i["mn"] and i["ue8m0"]]
+
+
+def _run_e8(p, C=None, workspace=None):
+    a = torch.from_numpy(p.A).cuda()
+    b = torch.from_numpy(p.B).cuda()
+    sfa = fp8bs.sfa_ue8m0_mn_major(torch.from_numpy(p.SA)).cuda()
+    sfb = fp8bs.sfa_ue8m0_mn_major(torch.from_numpy(p.SB)).cuda()
+    d = torch.full((p.G, p.M, p.N), float("nan"), dtype=torch.float32, device="cuda")
+    c = torch.from_numpy(C).cuda() if C is not None else None
+    fp8bs.fp8bs_k_grouped_tn_contiguous_ue8m0(a, sfa, b, sfb, d, list(p.ks), c=c,
+                                              workspace=workspace)
+    torch.cuda.synchronize()
+    return d.cpu().numpy()
+
+
+def _full_e8(p, what, C=None, workspace=None):
+    print(f"[gpu] k-grouped ue8m0 {what}: G={p.G} M={p.M} N={p.N} ks={list(p.ks)}", flush=True)
+    gpu = _run_e8(p, C, workspace)
+    _check(gpu, oracle.k_grouped(p.A, p.SA, p.B, p.SB, p.ks, C), p, C, what)
+
+
+@pytest.mark.parametrize("inst", E8_MN_INSTANCES)
+def test_ue8m0_every_instance(inst):
+    """Power-of-two scales as packed E8M0 exponents: per-row A and per-column B exponents
+    applied by the matrix core, no promotion step.  K = 5 chunks in one group, so a packed
+    word is partly used and a group starts inside a word."""
+    fp8bs.force_instance(inst)
+    p = synth.make_k_grouped(3, 80, 208, seed=990 + inst, counts=[100, 0, 600], pow2=True)
+    _full_e8(p, f"inst {inst}")
+
+
+def test_ue8m0_planner_split_k_and_addend():
+    p = synth.make_k_grouped(4, 96, 160, seed=995, counts=[128, 700, 0, 300], pow2=True)
+    C = np.random.default_rng(996).standard_normal((4, 96, 160)).astype(np.float32)
+    _full_e8(p, "planner, addend", C=C)
+    fp8bs.force_splits(3)
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+    _full_e8(p, "3 splits, addend", C=C, workspace=ws)
+
+
+def test_ue8m0_constant_operands_bit_exact():
+    ks = [256, 0, 384, 128]
+    p = synth.make_k_grouped(4, 48, 64, seed=997, counts=ks, pow2=True)
+    p.A[:] = 0x40
+    p.B[:] = 0xB0
+    p.SA[:] = 0.125
+    p.SB[:] = 4.0
+    gpu = _run_e8(p)
+    for g, k in enumerate(ks):
+        assert np.all(gpu[g] == np.float32(-k * 0.5)), g

@@ -124,3 +124,41 @@ def test_full_size_stored_forms_sampled(desc):
                      device="cuda")
     gpu = _run(p, form, workspace=ws)
     check_sampled(p, gpu, n_points=4096, seed=p.seed, what=desc["name"])
+
+
+E8_MN_INSTANCES = [i["instance"] for i in fp8bs.instances() if i["mn"] and i["ue8m0"]]
+
+
+def _run_e8(p, form, workspace=None):
+    A, B = synth.stored_operands(p, form)
+    a = torch.from_numpy(A).cuda()
+    b = torch.from_numpy(B).cuda()
+    sfa = fp8bs.sfa_ue8m0_mn_major(torch.from_numpy(p.SA)).cuda()
+    sfb = fp8bs.sfb_ue8m0(torch.from_numpy(np.ascontiguousarray(p.SB[0]))).cuda()
+    d = torch.full((p.M, p.N), SENTINEL, dtype=torch.int16, device="cuda")
+    getattr(fp8bs, f"fp8bs_dense_{form}_ue8m0")(a, sfa, b, sfb, d, workspace=workspace)
+    torch.cuda.synchronize()
+    return d.cpu().numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("form", FORMS)
+@pytest.mark.parametrize("inst", E8_MN_INSTANCES)
+def test_ue8m0_every_instance(form, inst):
+    """Power-of-two scales as packed E8M0 exponents with MN-major operands."""
+    fp8bs.force_instance(inst)
+    p = synth.make_dense(80, 208, 640, seed=870 + inst, pow2=True)
+    print(f"[gpu] form {form} ue8m0 inst {inst}", flush=True)
+    A, B = synth.stored_operands(p, form)
+    check_values(_run_e8(p, form), oracle.dense_layout(form, A, p.SA, B, p.SB[0]),
+                 f"{form} ue8m0 inst {inst}")
+
+
+@pytest.mark.parametrize("form", FORMS)
+def test_ue8m0_planner_and_split_k(form):
+    p = synth.make_dense(256, 400, 1536, seed=880, pow2=True)
+    A, B = synth.stored_operands(p, form)
+    ref = oracle.dense_layout(form, A, p.SA, B, p.SB[0])
+    check_values(_run_e8(p, form), ref, f"{form} ue8m0 planner")
+    fp8bs.force_splits(3)
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+    check_values(_run_e8(p, form, workspace=ws), ref, f"{form} ue8m0 3 splits")
