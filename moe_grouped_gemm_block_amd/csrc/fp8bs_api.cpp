@@ -141,7 +141,7 @@ int run(int layout, const void* a, const float* sfa, const void* b, const float*
     p.tiles = (int)pl.tiles;
     p.raster = pl.raster;
     p.splits = pl.splits;
-    p.units = (int)(pl.tiles * pl.splits);
+    p.units = (int)(pl.tiles * pl.splits * fp8bs::passes_per_tile(layout, pl.shape.block_m));
     p.ws = pl.splits > 1 ? (float*)ws : nullptr;
     p.c = want_c ? c : nullptr;
     p.sfb_ld = (int)fp8bs_get_sfa_ld(n);

@@ -146,7 +146,7 @@ struct Tile {
 // `raster` m-blocks sweep the n-blocks column by column.  Returns false when
 // the tile holds no valid row (masked: beyond masked_m; contiguous: padding).
 template <int BM, int BN, int LAYOUT>
-__device__ __forceinline__ bool tile_at(const GemmParams& p, int t, Tile& tl) {
+__device__ __forceinline__ bool tile_at(const GemmParams& p, int t, Tile& tl, int pass = 0) {
     int rest = t, g = 0;
     if (LAYOUT == kMasked || LAYOUT == kKGrouped) {
         const int per_slot = p.m_blocks * p.n_blocks;
@@ -168,9 +168,30 @@ __device__ __forceinline__ bool tile_at(const GemmParams& p, int t, Tile& tl) {
         if (tl.m0 >= v) return false;
         tl.row_limit = v;
     } else if (LAYOUT == kContiguous) {
-        const int e = p.grouped_layout[tl.m0];     // a 128-row block: one expert, then padding
-        if (e < 0 || e >= p.num_groups) return false;
-        g = e;
+        // A 128-row block holds one expert's rows, then padding; its first row names it.
+        auto expert = [&](int row) {
+            if (row >= p.m) return -1;
+            const int e = p.grouped_layout[row];
+            return (e >= 0 && e < p.num_groups) ? e : -1;
+        };
+        const int e0 = expert(tl.m0);
+        if constexpr (BM <= 128) {
+            if (e0 < 0) return false;
+            g = e0;
+        } else {
+            // A 256-row tile covers two blocks.  Pass 0 multiplies the tile with the first
+            // block's expert (the second's when the first is all padding); pass 1 with the
+            // second block's expert when that is a different one.  store_tile writes only
+            // the rows whose index is the pass's expert.
+            const int e1 = expert(tl.m0 + 128);
+            if (pass == 0) {
+                g = e0 >= 0 ? e0 : e1;
+                if (g < 0) return false;
+            } else {
+                if (e0 < 0 || e1 < 0 || e1 == e0) return false;
+                g = e1;
+            }
+        }
     }
     tl.g = g;
     return true;
@@ -194,9 +215,12 @@ template <int BM, int BN, int LAYOUT, typename OnEmpty = NoEmptyUnits>
 __device__ __forceinline__ bool next_unit(const GemmParams& p, int u, Unit& w,
                                           OnEmpty&& on_empty = OnEmpty{}) {
     const int kchunks = p.k / 128;
+    // contiguous layout, 256-row tiles: units are (pass, tile), pass-major, never split
+    constexpr bool PASSES = LAYOUT == kContiguous && BM > 128;
     for (; u < p.units; u += gridDim.x) {
-        const int s = u / p.tiles, t = u - s * p.tiles;
-        if (!tile_at<BM, BN, LAYOUT>(p, t, w.tl)) continue;
+        const int q = u / p.tiles, t = u - q * p.tiles;
+        const int s = PASSES ? 0 : q;
+        if (!tile_at<BM, BN, LAYOUT>(p, t, w.tl, PASSES ? q : 0)) continue;
         w.u = u;
         w.t = t;
         w.s = s;

@@ -112,6 +112,12 @@ struct Plan {
     int64_t workspace_bytes;    // bytes of workspace the launch uses (0 when splits == 1)
 };
 
+// Work units per tile and split: the contiguous layout with tiles taller than one
+// 128-row expert block runs each tile in two passes (one per expert it may hold).
+constexpr int passes_per_tile(int layout, int block_m) {
+    return layout == kContiguous && block_m > 128 ? 2 : 1;
+}
+
 // Workspace bytes a launch of `shape` with `splits` K splits needs.
 int64_t split_workspace_bytes(const InstanceShape& shape, int64_t tiles, int splits);
 

@@ -129,8 +129,9 @@ int64_t tile_count(const Request& r, const InstanceShape& s) {
 bool instance_fits(const Request& r, const InstanceShape& s) {
     // MN-major operands (nn / tn / tt, K-grouped) need an instance compiled for them
     if ((r.form != kFormNT || r.layout == kKGrouped) && !s.mn) return false;
-    // a contiguous-layout tile must not straddle two 128-row expert blocks
-    return !(r.layout == kContiguous && 128 % s.block_m != 0);
+    // a contiguous-layout tile lies inside one 128-row expert block, or covers exactly two
+    // (then each tile runs in two passes, one per expert)
+    return !(r.layout == kContiguous && 128 % s.block_m != 0 && s.block_m != 256);
 }
 
 // Estimated time of instance s with `splits` K splits; < 0 when infeasible.
@@ -146,9 +147,12 @@ double estimate(const Request& r, const InstanceShape& s, int splits) {
     // group's chunks are empty units -- but the estimate uses the mean group)
     const int max_splits = kg ? (r.k / 128 > 1 ? r.k / 128 : 1) : kchunks;
     if (splits < 1 || splits > max_splits) return -1.0;
+    // two-pass contiguous tiles are never split
+    const int passes = passes_per_tile(r.layout, s.block_m);
+    if (passes > 1 && splits > 1) return -1.0;
     const int64_t tiles = tile_count(r, s);
     // unit indices (and unit + grid) stay well inside int
-    if (tiles * splits > 0x7f000000) return -1.0;
+    if (tiles * splits * passes_per_tile(r.layout, s.block_m) > 0x7f000000) return -1.0;
     if (split_workspace_bytes(s, tiles, splits) > r.workspace_bytes) return -1.0;
     const int64_t n_blocks = ((int64_t)r.n + s.block_n - 1) / s.block_n;
     double eff_m_blocks = (double)((r.eff_rows + s.block_m - 1) / s.block_m);
@@ -159,7 +163,9 @@ double estimate(const Request& r, const InstanceShape& s, int splits) {
         eff_m_blocks = sum / r.spread;
     }
     const double eff_tiles = (r.layout == kMasked || kg ? r.G : 1) * eff_m_blocks * n_blocks;
-    const int64_t units = tiles * splits;
+    // a second pass runs only for a tile whose two blocks hold different experts: about
+    // one tile in 32 for segments of thousands of rows
+    const int64_t units = passes > 1 ? tiles + (tiles + 31) / 32 : tiles * splits;
     const int64_t per_cu = (units + r.num_cus - 1) / r.num_cus;
     const int64_t chunks_per_unit = (kchunks + splits - 1) / splits;
     // Operands stream from HBM when a byte of A or B feeds fewer flops than the chip's
@@ -195,7 +201,7 @@ void fill_launch(int i, const Request& r, int splits, Plan* out) {
     const int64_t m_blocks = (r.m + s.block_m - 1) / s.block_m;
     const int64_t tiles = tile_count(r, s);
     const int64_t slots = (int64_t)r.num_cus * s.wg_per_cu;
-    const int64_t units = tiles * splits;
+    const int64_t units = tiles * splits * passes_per_tile(r.layout, s.block_m);
     // kStaged: persistent grid; kStreamB: one workgroup per unit
     int64_t grid = (s.kind == kStreamB || units < slots) ? units : slots;
     if (grid < 1) grid = 1;

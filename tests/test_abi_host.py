@@ -78,7 +78,7 @@ def test_planner_is_deterministic_and_consistent():
             assert 1 <= q1["grid"] <= q1["tiles"]
             assert q1["tiles"] == fp8bs.count_tiles(layout, m, d["N"], g, q1["block_m"], q1["block_n"])
             if layout == 1:
-                assert 128 % q1["block_m"] == 0
+                assert 128 % q1["block_m"] == 0 or q1["block_m"] == 256
             assert q1["threads"] == 64 * q1["waves_m"] * q1["waves_n"]
 
 

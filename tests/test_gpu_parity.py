@@ -44,7 +44,9 @@ def _run_and_check(p, what, workspace=True):
 def _instances(layout):
     out = []
     for inst in fp8bs.instances():
-        if layout == fp8bs.LAYOUT_CONTIGUOUS and 128 % inst["block_m"] != 0:
+        # contiguous: a tile inside one 128-row expert block, or two blocks (two passes)
+        if layout == fp8bs.LAYOUT_CONTIGUOUS and 128 % inst["block_m"] != 0 and \
+                inst["block_m"] != 256:
             continue
         out.append(inst["instance"])
     return out
@@ -70,7 +72,7 @@ def test_dense_planner_shapes(M, N, K):
 @pytest.mark.parametrize("inst", range(N_INST))
 def test_contiguous_every_instance(inst):
     if inst not in _instances(fp8bs.LAYOUT_CONTIGUOUS):
-        pytest.skip("block_m does not divide the 128-row alignment")
+        pytest.skip("block_m neither divides the 128-row alignment nor spans two blocks")
     fp8bs.force_instance(inst)
     p = synth.make_contiguous(4, 300, 384, seed=31 + inst, counts=[200, 0, 1, 129])
     _run_and_check(p, f"contiguous inst {inst}", workspace=False)
@@ -113,10 +115,15 @@ def test_dense_split_k_every_instance(inst, splits):
 @pytest.mark.parametrize("inst", range(N_INST))
 def test_contiguous_split_k_every_instance(inst):
     if inst not in _instances(fp8bs.LAYOUT_CONTIGUOUS):
-        pytest.skip("block_m does not divide the 128-row alignment")
+        pytest.skip("block_m neither divides the 128-row alignment nor spans two blocks")
     fp8bs.force_instance(inst)
     fp8bs.force_splits(3)
     p = synth.make_contiguous(4, 300, 768, seed=91 + inst, counts=[200, 0, 1, 129])
+    if fp8bs.instances()[inst]["block_m"] > 128:
+        # two-pass tiles (two expert blocks per tile) are never split: the pin is refused
+        with pytest.raises(fp8bs.FP8BSError):
+            _run_and_check(p, f"contiguous inst {inst} splits 3")
+        return
     _run_and_check(p, f"contiguous inst {inst} splits 3")
 
 

@@ -72,8 +72,9 @@ def test_dense_every_instance(inst):
 
 @pytest.mark.parametrize("inst", E8_CAPABLE)
 def test_contiguous_every_instance(inst):
-    if 128 % fp8bs.instances()[inst]["block_m"] != 0:
-        pytest.skip("block_m does not divide the 128-row alignment")
+    bm = fp8bs.instances()[inst]["block_m"]
+    if 128 % bm != 0 and bm != 256:
+        pytest.skip("block_m neither divides the 128-row alignment nor spans two blocks")
     fp8bs.force_instance(inst)
     p = synth.make_contiguous(4, 300, 1152, seed=521 + inst, counts=[200, 0, 1, 129], pow2=True)
     _check(p, f"contiguous inst {inst}")
