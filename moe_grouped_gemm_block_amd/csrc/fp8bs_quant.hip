@@ -89,11 +89,35 @@ __device__ __forceinline__ void load8(const void* x, int64_t e, float (&v)[8]) {
     }
 }
 
+// Four values to four e4m3 codes with gfx950's conversion instruction (v_cvt_pk_fp8_f32,
+// OCP e4m3, round to nearest even).  For every finite input of magnitude at most 448 it
+// gives the code enc_e4m3 gives -- checked on MI355X against every code value, every tie
+// between neighbouring codes, the values one ulp either side of each tie and two million
+// random values -- so the quantisers stay bit-exact with the definition.
+__device__ __forceinline__ uint32_t cvt4_e4m3(float a, float b, float c, float d) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+    return (uint32_t)w;
+}
+
 __device__ __forceinline__ uint2 quantise8(const float (&v)[8], float inv) {
+    float s[8];
+    bool nan = false;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        s[i] = clamp448(v[i] * inv);
+        nan |= s[i] != s[i];
+    }
+    uint2 out;
+    if (!nan) {
+        out.x = cvt4_e4m3(s[0], s[1], s[2], s[3]);
+        out.y = cvt4_e4m3(s[4], s[5], s[6], s[7]);
+        return out;
+    }
+    // a NaN input: the software encoder, which keeps the input's sign on the NaN code
     uint32_t c[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) c[i] = enc_e4m3(clamp448(v[i] * inv));
-    uint2 out;
+    for (int i = 0; i < 8; ++i) c[i] = enc_e4m3(s[i]);
     out.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
     out.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
     return out;

@@ -142,3 +142,20 @@ def test_quantiser_validation():
     assert lib.fp8bs_quantize_1x128(ptr, 0, ptr, ptr, 1, 0, 128, None) == 0      # nothing to do
     assert lib.fp8bs_quantize_128x128(ptr, 0, ptr, ptr, 1, 0, 128, None) == 1
     torch.cuda.synchronize()
+
+
+def test_nan_inputs_keep_their_sign_on_the_nan_code():
+    """NaN never raises a block's maximum and becomes the NaN code with its sign; the rest
+    of the group (converted by the hardware instruction) stays bit-exact."""
+    rng = np.random.default_rng(500)
+    x = rng.standard_normal((3, 256)).astype(np.float32)
+    x[0, 5] = np.nan
+    x[1, 130] = -np.nan
+    x[2, 0] = np.float32(np.copysign(np.nan, -1.0))
+    q, sfa = fp8bs.quantize_1x128(torch.from_numpy(x).cuda())
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.quant_1x128(x)
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+    assert (q_ref[0, 5] & 0x7F) == 0x7F and (q_ref[2, 0] == 0xFF)
+    s_log, _ = _sfa_logical(sfa, 3)
+    assert np.array_equal(s_log.view(np.uint32), s_ref.view(np.uint32))
