@@ -1128,36 +1128,76 @@ __global__ void __launch_bounds__(64 * NW) fp8bs_stream_kernel(GemmParams p) {
     }
 }
 
-// Split-K reduction: for every tile with valid rows, the FP32 partials of its K splits
-// are added in split order 0, 1, ..., S-1 (the same order whatever order the splits
-// finished in, so results are reproducible), rounded to BF16 and stored at valid rows
-// and columns exactly as the GEMM kernel's own epilogue would.
+// Split-K reduction, one thread per four outputs of a partial tile (every workgroup of
+// 256 threads covers 1024 outputs of one tile, so the whole reduction runs on
+// tiles * BM*BN/1024 workgroups): the FP32 partials of the tile's K splits are added in
+// split order 0, 1, ..., S-1 (the same order whatever order the splits finished in, so
+// results are reproducible), then written -- BF16, or FP32 for the K-grouped layout, with
+// C added when given -- at valid rows and columns.  Partial element e of a tile is
+// accumulator (i, j) of lane `lane` of wavefront `wave` in the GEMM kernel,
+// e = ((wave * TM + i) * TN + j) * 64 + lane (partial_index), which fixes its row and
+// columns exactly as store_tile does.
+constexpr int kReduceThreads = 256;
+
+template <int BM, int BN>
+constexpr int reduce_groups_per_tile() {
+    return (BM * BN / 4 + kReduceThreads - 1) / kReduceThreads;
+}
+
 template <int BM, int BN, int WM, int WN, int LAYOUT, bool AMN = false>
-__global__ void __launch_bounds__(64 * WM * WN) fp8bs_splitk_reduce(GemmParams p) {
+__global__ void __launch_bounds__(kReduceThreads) fp8bs_splitk_reduce(GemmParams p) {
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int TM = WTM / 16, TN = WTN / 16;
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wm = wave / WN, wn = wave % WN;
-    const int lj = lane & 15, kq = lane >> 4;
+    constexpr int V = BM * BN / 4;                    // f32x4 per partial tile
+    constexpr int PER_TILE = reduce_groups_per_tile<BM, BN>();
+    const int t = blockIdx.x / PER_TILE;
+    const int e = (blockIdx.x - t * PER_TILE) * kReduceThreads + threadIdx.x;
+    if (t >= p.tiles || e >= V) return;
+    Tile tl;
+    if (!tile_at<BM, BN, LAYOUT>(p, t, tl)) return;
+    const f32x4* ws = (const f32x4*)(p.ws + (int64_t)t * p.splits * (BM * BN)) + e;
+    f32x4 acc = ws[0];
+    for (int s = 1; s < p.splits; ++s) acc += ws[(int64_t)s * V];
+
+    const int lane = e & 63, rest = e >> 6;
+    const int j = rest % TN, i = (rest / TN) % TM, wave = rest / (TM * TN);
+    const int wm = wave / WN, wn = wave % WN, lj = lane & 15, kq = lane >> 4;
     const int flip = (TM > 1 && !AMN) ? (lj >> 3) : 0;
-    for (int t = blockIdx.x; t < p.tiles; t += gridDim.x) {
-        Tile tl;
-        if (!tile_at<BM, BN, LAYOUT>(p, t, tl)) continue;
-        f32x4 acc[TM][TN];
-        const f32x4* ws = (const f32x4*)(p.ws + (int64_t)t * p.splits * (BM * BN));
+    const int row = tl.m0 + wm * WTM + (AMN ? 16 * i + lj : TM * lj + (i ^ flip));
+    const int col = tl.n0 + wn * WTN + 16 * j + 4 * kq;
+    if (row >= tl.row_limit) return;
+    if (LAYOUT == kContiguous && p.grouped_layout[row] != tl.g) return;
+    const int64_t slot = (LAYOUT == kMasked || LAYOUT == kKGrouped)
+                             ? (int64_t)tl.g * p.m * p.n : (int64_t)0;
+    const int64_t off = slot + (int64_t)row * p.n + col;
+    const bool vec = (p.n & 3) == 0 && col + 3 < p.n;
+    if (p.c) {                                        // D = C + A B^T
+        if (vec) {
+            acc += *(const f32x4*)(p.c + off);
+        } else {
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int j = 0; j < TN; ++j) acc[i][j] = ws[partial_index<TM, TN>(wave, i, j, lane)];
-        for (int s = 1; s < p.splits; ++s) {
-            const f32x4* wss = ws + (int64_t)s * (BM * BN / 4);
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j) acc[i][j] += wss[partial_index<TM, TN>(wave, i, j, lane)];
+            for (int v = 0; v < 4; ++v)
+                if (col + v < p.n) acc[v] += p.c[off + v];
         }
-        store_tile<TM, TN, WTM, WTN, LAYOUT, AMN>(p, tl, acc, wm, wn, lj, kq, flip);
+    }
+    if constexpr (LAYOUT == kKGrouped) {
+        float* d = (float*)(void*)p.d + off;
+        if (vec) {
+            *(f32x4*)d = acc;
+        } else {
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                if (col + v < p.n) d[v] = acc[v];
+        }
+    } else {
+        uint16_t* d = p.d + off;
+        if (vec) {
+            *(uint2*)d = uint2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+        } else {
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                if (col + v < p.n) d[v] = to_bf16(acc[v]);
+        }
     }
 }
 
@@ -1174,6 +1214,7 @@ struct InstanceEntry {
     KernelFn reduce_kg;
     KernelFn fn_form_e8[4];    // the same with packed UE8M0 scales (null: not compiled)
     KernelFn fn_kg_e8;
+    int reduce_groups;         // split-K reduction workgroups per tile
 };
 
 template <int KIND, int BM, int BN, int WM, int WN, int NS, int LAYOUT, int SCALE>
@@ -1231,7 +1272,8 @@ constexpr KernelFn mn_fn() {
       mn_fn<KIND, BM, BN, WM, WN, NS, MN, kDense, false, true, false, E8>(),                \
       mn_fn<KIND, BM, BN, WM, WN, NS, MN, kDense, true, true, false, E8>(),                 \
       mn_fn<KIND, BM, BN, WM, WN, NS, MN, kDense, true, false, false, E8>()},               \
-     mn_fn<KIND, BM, BN, WM, WN, NS, MN, kKGrouped, true, true, false, E8>()},
+     mn_fn<KIND, BM, BN, WM, WN, NS, MN, kKGrouped, true, true, false, E8>(),               \
+     reduce_groups_per_tile<BM, BN>()},
 const InstanceEntry kEntries[] = {
 #include "fp8bs_instances.inc"
 };
@@ -1264,9 +1306,10 @@ int launch_instance(const Plan& plan, int layout, int scale_mode, const GemmPara
     hipError_t err = hipLaunchKernel((const void*)fn, dim3((unsigned)plan.grid),
                                      dim3(e.threads), argv, 0, stream);
     if (err != hipSuccess || p.splits == 1) return (int)err;
-    // one workgroup per tile (tiles without valid rows return at once)
-    return (int)hipLaunchKernel((const void*)reduce, dim3((unsigned)p.tiles),
-                                dim3(e.threads), argv, 0, stream);
+    // reduce_groups workgroups per tile (tiles without valid rows return at once)
+    return (int)hipLaunchKernel((const void*)reduce,
+                                dim3((unsigned)(p.tiles * (int64_t)e.reduce_groups)),
+                                dim3(kReduceThreads), argv, 0, stream);
 }
 
 }  // namespace fp8bs
