@@ -6,7 +6,11 @@ run once, back to back, on one stream (default: the dense prefill sweep,
 M = 4096 x six (N, K) shapes).  Inputs are synthetic, seeded, and resident in
 HBM before timing starts.  Prints one JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--family F] [--graph] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--family F] [--eager] [--no-cpu-baseline]
+
+The K timed steps are captured in one HIP graph and replayed once (--eager: launched
+one by one from Python, which also times the host's per-call overhead); each shape's
+launch times come from an event pair around every launch of a second, eager pass.
 """
 from __future__ import annotations
 
@@ -82,10 +86,10 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=1536,
                     help="rows of D per shape the oracle computes for the CPU baseline")
     ap.add_argument("--per-shape-out", default="", help="also write per-shape results here")
-    ap.add_argument("--graph", action="store_true",
-                    help="capture the K timed steps (and K calls of each shape) in HIP graphs "
-                         "and time one replay: for families of short kernels, where per-call "
-                         "host overhead would otherwise be timed")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch the K timed steps one call at a time from Python instead of "
+                         "replaying them as one captured graph")
+    ap.add_argument("--graph", action="store_true", help="(the default; kept for old command lines)")
     args = ap.parse_args()
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, args.family)
@@ -206,10 +210,30 @@ def main():
     stream = torch.cuda.current_stream(dev)
     step_start = torch.cuda.Event(enable_timing=True)
     step_end = torch.cuda.Event(enable_timing=True)
-    if args.graph:
+    def eager_steps():
+        """K steps launched one by one, an event pair around every launch; returns the
+        per-launch times (ms) per shape and the wall time."""
+        ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in problems] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        step_start.record(stream)
+        for s_ in range(args.steps):
+            for i, q in enumerate(problems):
+                ev[s_][i][0].record(stream)
+                launch(q)
+                ev[s_][i][1].record(stream)
+        step_end.record(stream)
+        torch.cuda.synchronize()
+        w = time.perf_counter() - w0
+        return [[ev[s_][i][0].elapsed_time(ev[s_][i][1]) for s_ in range(args.steps)]
+                for i in range(len(problems))], w
+
+    if not args.eager:
         # The K timed steps are captured as one graph (K back-to-back steps) and replayed
-        # once, so no per-replay launch gap is timed; per shape, a graph of K calls of
-        # that shape alone gives its average launch time.
+        # once, so the host's per-call overhead is not timed.  Events cannot be recorded
+        # inside a captured graph here, so per-launch times come from a second pass of K
+        # steps launched one by one with an event pair around every launch.
         side = torch.cuda.Stream(dev)
         side.wait_stream(stream)
         with torch.cuda.stream(side):
@@ -217,13 +241,6 @@ def main():
                 launch(q)
         stream.wait_stream(side)
         torch.cuda.synchronize()
-        shape_graphs = []
-        for q in problems:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                for _ in range(args.steps):
-                    launch(q)
-            shape_graphs.append(g)
         step_graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(step_graph):
             for _ in range(args.steps):
@@ -240,33 +257,11 @@ def main():
         step_end.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - wall0
-        shape_ms = []
-        for g in shape_graphs:
-            g.replay()                                  # first replay untimed
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            g.replay()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            shape_ms.append([e0.elapsed_time(e1) / args.steps] * args.steps)
+        total_ms = step_start.elapsed_time(step_end)
+        shape_ms, _ = eager_steps()
     else:
-        ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in problems] for _ in range(args.steps)]
-        torch.cuda.synchronize()
-        wall0 = time.perf_counter()
-        step_start.record(stream)
-        for s in range(args.steps):
-            for i, q in enumerate(problems):
-                ev[s][i][0].record(stream)
-                launch(q)
-                ev[s][i][1].record(stream)
-        step_end.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - wall0
-        shape_ms = [[ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]
-                    for i in range(len(problems))]
-    total_ms = step_start.elapsed_time(step_end)
+        shape_ms, wall = eager_steps()
+        total_ms = step_start.elapsed_time(step_end)
     ms_per_step = total_ms / args.steps
 
     flops_step = sum(q["p"].flops() for q in problems)
@@ -323,8 +318,9 @@ def main():
         "config": {"workload": FAMILY_NAMES[args.family], "family": args.family,
                    "shapes": [q["desc"]["name"] for q in problems],
                    "gflop_per_step": flops_step / 1e9,
-                   "timing": ("one graph of K steps, replayed once" if args.graph
-                              else "eager launches")},
+                   "timing": ("step: one graph of K steps, replayed once; per launch: event "
+                              "pairs around each launch in a second, eager pass of K steps"
+                              if not args.eager else "eager launches")},
         "roofline": roof, "cpu_baseline": cpu,
         "per_shape": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in s.items()}
                       for s in per_shape],
