@@ -16,6 +16,7 @@ Build it with ``python -m moe_grouped_gemm_block_amd.build``.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from typing import Optional
@@ -220,6 +221,10 @@ def _torch():
 
 def _dev_ptr(t, name, dtypes, ndim=None):
     torch = _torch()
+    # common case first: a contiguous device tensor of an accepted dtype
+    if (type(t) is torch.Tensor and t.is_cuda and t.dtype in dtypes and t.is_contiguous()
+            and (ndim is None or t.dim() == ndim)):
+        return ctypes.c_void_p(t.data_ptr())
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.device.type != "cuda":
@@ -233,19 +238,45 @@ def _dev_ptr(t, name, dtypes, ndim=None):
     return ctypes.c_void_p(t.data_ptr())
 
 
+_DTYPES = {}
+
+
 def _fp8_dtypes():
-    torch = _torch()
-    return (torch.uint8, torch.float8_e4m3fn)
+    d = _DTYPES.get("fp8")
+    if d is None:
+        torch = _torch()
+        d = _DTYPES["fp8"] = (torch.uint8, torch.float8_e4m3fn)
+    return d
 
 
 def _bf16_dtypes():
+    d = _DTYPES.get("bf16")
+    if d is None:
+        torch = _torch()
+        d = _DTYPES["bf16"] = (torch.bfloat16, torch.int16, torch.uint16)
+    return d
+
+
+_NO_SWITCH = contextlib.nullcontext()
+
+
+def _on_device(t):
+    """Context that makes t's device current (nothing to do when it already is)."""
     torch = _torch()
-    return (torch.bfloat16, torch.int16, torch.uint16)
+    idx = t.get_device()
+    if idx == torch.cuda.current_device():
+        return _NO_SWITCH
+    return torch.cuda.device(idx)
 
 
 def _stream_handle(stream, device):
+    """Raw HIP stream handle: the given torch stream, or the device's current stream."""
     torch = _torch()
     if stream is None:
+        raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        if raw is not None:
+            return ctypes.c_void_p(raw(device.index if device.index is not None
+                                       else torch.cuda.current_device()))
         stream = torch.cuda.current_stream(device)
     return ctypes.c_void_p(stream.cuda_stream)
 
@@ -277,7 +308,7 @@ def _workspace(ws, layout, m, n, k, g, expected_m, stream, device):
         nbytes = workspace_size(layout, m, n, k, g, expected_m)
         if nbytes == 0:
             return ctypes.c_void_p(None), 0, None
-        with torch.cuda.stream(stream):
+        with torch.cuda.stream(_stream(stream, device)):
             ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
     ptr = _dev_ptr(ws, "workspace", (torch.uint8,), 1)
     return ptr, ws.numel(), ws
@@ -341,7 +372,7 @@ def fp8bs_dense_nt(a, sfa, b, sfb, d, stream=None):
     a: e4m3 [m][k]; sfa: f32 MN-major [k/128][ld(m)]; b: e4m3 [n][k];
     sfb: f32 [ceil(n/128)][k/128]; d: bf16 [m][n] (written)."""
     args, m, n, k = _dense_args(a, sfa, b, sfb, d)
-    with _torch().cuda.device(a.device):
+    with _on_device(a):
         st = _load().fp8bs_dense_nt(*args, m, n, k, _stream_handle(stream, a.device))
     _check(st, "fp8bs_dense_nt")
 
@@ -349,17 +380,17 @@ def fp8bs_dense_nt(a, sfa, b, sfb, d, stream=None):
 def fp8bs_dense_nt_ws(a, sfa, b, sfb, d, workspace=None, stream=None):
     """fp8bs_dense_nt with a split-K workspace (uint8 device tensor, or None to allocate)."""
     args, m, n, k = _dense_args(a, sfa, b, sfb, d)
-    with _torch().cuda.device(a.device):
-        s = _stream(stream, a.device)
+    with _on_device(a):
+        s = stream
         wp, wb, _keep = _workspace(workspace, LAYOUT_DENSE, m, n, k, 1, 0, s, a.device)
-        st = _load().fp8bs_dense_nt_ws(*args, m, n, k, wp, wb, ctypes.c_void_p(s.cuda_stream))
+        st = _load().fp8bs_dense_nt_ws(*args, m, n, k, wp, wb, _stream_handle(s, a.device))
     _check(st, "fp8bs_dense_nt_ws")
 
 
 def fp8bs_grouped_contiguous_nt(a, sfa, b, sfb, d, grouped_layout, stream=None):
     """Contiguous MoE layout: a [m_total][k], b [g][n][k], grouped_layout int32 [m_total]."""
     args, m, n, k, g = _contiguous_args(a, sfa, b, sfb, d, grouped_layout)
-    with _torch().cuda.device(a.device):
+    with _on_device(a):
         st = _load().fp8bs_grouped_contiguous_nt(*args, m, n, k, g, _stream_handle(stream, a.device))
     _check(st, "fp8bs_grouped_contiguous_nt")
 
@@ -367,18 +398,18 @@ def fp8bs_grouped_contiguous_nt(a, sfa, b, sfb, d, grouped_layout, stream=None):
 def fp8bs_grouped_contiguous_nt_ws(a, sfa, b, sfb, d, grouped_layout, workspace=None, stream=None):
     """fp8bs_grouped_contiguous_nt with a split-K workspace."""
     args, m, n, k, g = _contiguous_args(a, sfa, b, sfb, d, grouped_layout)
-    with _torch().cuda.device(a.device):
-        s = _stream(stream, a.device)
+    with _on_device(a):
+        s = stream
         wp, wb, _keep = _workspace(workspace, LAYOUT_CONTIGUOUS, m, n, k, g, 0, s, a.device)
         st = _load().fp8bs_grouped_contiguous_nt_ws(*args, m, n, k, g, wp, wb,
-                                                    ctypes.c_void_p(s.cuda_stream))
+                                                    _stream_handle(s, a.device))
     _check(st, "fp8bs_grouped_contiguous_nt_ws")
 
 
 def fp8bs_grouped_masked_nt(a, sfa, b, sfb, d, masked_m, expected_m: int = 0, stream=None):
     """Masked MoE layout: a [g][max_m][k], b [g][n][k], d [g][max_m][n], masked_m int32 [g]."""
     args, g, max_m, n, k = _masked_args(a, sfa, b, sfb, d, masked_m)
-    with _torch().cuda.device(a.device):
+    with _on_device(a):
         st = _load().fp8bs_grouped_masked_nt(*args, g, max_m, int(expected_m), n, k,
                                              _stream_handle(stream, a.device))
     _check(st, "fp8bs_grouped_masked_nt")
@@ -388,12 +419,12 @@ def fp8bs_grouped_masked_nt_ws(a, sfa, b, sfb, d, masked_m, expected_m: int = 0,
                                stream=None):
     """fp8bs_grouped_masked_nt with a split-K workspace."""
     args, g, max_m, n, k = _masked_args(a, sfa, b, sfb, d, masked_m)
-    with _torch().cuda.device(a.device):
-        s = _stream(stream, a.device)
+    with _on_device(a):
+        s = stream
         wp, wb, _keep = _workspace(workspace, LAYOUT_MASKED, max_m, n, k, g, int(expected_m), s,
                                    a.device)
         st = _load().fp8bs_grouped_masked_nt_ws(*args, g, max_m, int(expected_m), n, k, wp, wb,
-                                                ctypes.c_void_p(s.cuda_stream))
+                                                _stream_handle(s, a.device))
     _check(st, "fp8bs_grouped_masked_nt_ws")
 
 
@@ -431,7 +462,7 @@ def fp8bs_quantize_1x128(x, q, sfa, stream=None):
         raise ValueError("q must have x's shape")
     if k % 128 == 0 and sfa.numel() != G * (k // 128) * get_sfa_ld(rows):
         raise ValueError("sfa must hold [G][k/128][ld(rows)] floats")
-    with torch.cuda.device(x.device):
+    with _on_device(x):
         st = _load().fp8bs_quantize_1x128(xp, _x_dtype(x), qp, sp, G, rows, k,
                                           _stream_handle(stream, x.device))
     _check(st, "fp8bs_quantize_1x128")
@@ -452,7 +483,7 @@ def fp8bs_quantize_128x128(x, q, sfb, stream=None):
         raise ValueError("q must have x's shape")
     if k % 128 == 0 and sfb.numel() != G * ((n + 127) // 128) * (k // 128):
         raise ValueError("sfb must hold [G][ceil(n/128)][k/128] floats")
-    with torch.cuda.device(x.device):
+    with _on_device(x):
         st = _load().fp8bs_quantize_128x128(xp, _x_dtype(x), qp, sp, G, n, k,
                                             _stream_handle(stream, x.device))
     _check(st, "fp8bs_quantize_128x128")
@@ -557,7 +588,7 @@ def fp8bs_dense_nt_ue8m0(a, sfa, b, sfb, d, workspace=None, stream=None):
         raise ValueError("shape mismatch between a, b and d")
     sap, sbp = _ue8m0_checks(sfa, sfb, 1, 1, m, n, k)
     wp, wb = _opt_workspace(workspace)
-    with torch.cuda.device(a.device):
+    with _on_device(a):
         st = _load().fp8bs_dense_nt_ue8m0(ap, sap, bp, sbp, dp, m, n, k, wp, wb,
                                           _stream_handle(stream, a.device))
     _check(st, "fp8bs_dense_nt_ue8m0")
@@ -577,7 +608,7 @@ def fp8bs_grouped_contiguous_nt_ue8m0(a, sfa, b, sfb, d, grouped_layout, workspa
         raise ValueError("shape mismatch between a, b, d and grouped_layout")
     sap, sbp = _ue8m0_checks(sfa, sfb, 1, g, m, n, k)
     wp, wb = _opt_workspace(workspace)
-    with torch.cuda.device(a.device):
+    with _on_device(a):
         st = _load().fp8bs_grouped_contiguous_nt_ue8m0(ap, sap, bp, sbp, dp, lp, m, n, k, g, wp,
                                                        wb, _stream_handle(stream, a.device))
     _check(st, "fp8bs_grouped_contiguous_nt_ue8m0")
@@ -597,7 +628,7 @@ def fp8bs_grouped_masked_nt_ue8m0(a, sfa, b, sfb, d, masked_m, expected_m: int =
         raise ValueError("shape mismatch between a, b, d and masked_m")
     sap, sbp = _ue8m0_checks(sfa, sfb, g, g, max_m, n, k)
     wp, wb = _opt_workspace(workspace)
-    with torch.cuda.device(a.device):
+    with _on_device(a):
         st = _load().fp8bs_grouped_masked_nt_ue8m0(ap, sap, bp, sbp, dp, mp, g, max_m,
                                                    int(expected_m), n, k, wp, wb,
                                                    _stream_handle(stream, a.device))
@@ -617,11 +648,11 @@ def fp8bs_dense_nt_c(a, sfa, b, sfb, c, d, workspace=None, stream=None):
     """D = bf16(C + A B^T): fp8bs_dense_nt_ws with an FP32 addend c [m][n]."""
     args, m, n, k = _dense_args(a, sfa, b, sfb, d)
     cp = _addend(c, d)
-    with _torch().cuda.device(a.device):
-        s = _stream(stream, a.device)
+    with _on_device(a):
+        s = stream
         wp, wb, _keep = _workspace(workspace, LAYOUT_DENSE, m, n, k, 1, 0, s, a.device)
         st = _load().fp8bs_dense_nt_c(*args[:4], cp, args[4], m, n, k, wp, wb,
-                                      ctypes.c_void_p(s.cuda_stream))
+                                      _stream_handle(s, a.device))
     _check(st, "fp8bs_dense_nt_c")
 
 
@@ -630,11 +661,11 @@ def fp8bs_grouped_contiguous_nt_c(a, sfa, b, sfb, c, d, grouped_layout, workspac
     """Contiguous MoE layout with an FP32 addend c [m_total][n]."""
     args, m, n, k, g = _contiguous_args(a, sfa, b, sfb, d, grouped_layout)
     cp = _addend(c, d)
-    with _torch().cuda.device(a.device):
-        s = _stream(stream, a.device)
+    with _on_device(a):
+        s = stream
         wp, wb, _keep = _workspace(workspace, LAYOUT_CONTIGUOUS, m, n, k, g, 0, s, a.device)
         st = _load().fp8bs_grouped_contiguous_nt_c(*args[:4], cp, args[4], args[5], m, n, k, g,
-                                                   wp, wb, ctypes.c_void_p(s.cuda_stream))
+                                                   wp, wb, _stream_handle(s, a.device))
     _check(st, "fp8bs_grouped_contiguous_nt_c")
 
 
@@ -643,13 +674,13 @@ def fp8bs_grouped_masked_nt_c(a, sfa, b, sfb, c, d, masked_m, expected_m: int = 
     """Masked MoE layout with an FP32 addend c [g][max_m][n]."""
     args, g, max_m, n, k = _masked_args(a, sfa, b, sfb, d, masked_m)
     cp = _addend(c, d)
-    with _torch().cuda.device(a.device):
-        s = _stream(stream, a.device)
+    with _on_device(a):
+        s = stream
         wp, wb, _keep = _workspace(workspace, LAYOUT_MASKED, max_m, n, k, g, int(expected_m), s,
                                    a.device)
         st = _load().fp8bs_grouped_masked_nt_c(*args[:4], cp, args[4], args[5], g, max_m,
                                                int(expected_m), n, k, wp, wb,
-                                               ctypes.c_void_p(s.cuda_stream))
+                                               _stream_handle(s, a.device))
     _check(st, "fp8bs_grouped_masked_nt_c")
 
 
@@ -678,10 +709,10 @@ def _dense_form(form, a, sfa, b, sfb, c, d, workspace, stream, e8=False):
     cp = _addend(c, d) if c is not None else ctypes.c_void_p(None)
     code = {"nn": LAYOUT_DENSE_NN, "tn": LAYOUT_DENSE_TN, "tt": LAYOUT_DENSE_TT}[form]
     name = "fp8bs_dense_" + form + ("_ue8m0" if e8 else "")
-    with torch.cuda.device(a.device):
-        s = _stream(stream, a.device)
+    with _on_device(a):
+        s = stream
         wp, wb, _keep = _workspace(workspace, code, m, n, k, 1, 0, s, a.device)
-        st = getattr(_load(), name)(*args, cp, dp, m, n, k, wp, wb, ctypes.c_void_p(s.cuda_stream))
+        st = getattr(_load(), name)(*args, cp, dp, m, n, k, wp, wb, _stream_handle(s, a.device))
     _check(st, name)
 
 
@@ -755,10 +786,10 @@ def _k_grouped(a, sfa, b, sfb, d, ks, c, workspace, stream, e8):
     dp = _dev_ptr(d, "d", (torch.float32,), 3)
     cp = _addend(c, d) if c is not None else ctypes.c_void_p(None)
     ks_host = (ctypes.c_int32 * max(g, 1))(*sizes)
-    with torch.cuda.device(a.device):
-        s = _stream(stream, a.device)
+    with _on_device(a):
+        s = stream
         wp, wb, _keep = _workspace(workspace, LAYOUT_K_GROUPED, m, n, k_total, g, 0, s, a.device)
         name = "fp8bs_k_grouped_tn_contiguous" + ("_ue8m0" if e8 else "")
         st = getattr(_load(), name)(*args, cp, dp, ks_host, g, m, n, k_total, wp, wb,
-                                    ctypes.c_void_p(s.cuda_stream))
+                                    _stream_handle(s, a.device))
     _check(st, name)

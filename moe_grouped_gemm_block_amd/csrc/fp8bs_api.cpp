@@ -67,6 +67,27 @@ void format_plan(const fp8bs::Plan& pl, int layout, int form, int64_t m, int n, 
              (long long)pl.grid, pl.raster, pl.instance);
 }
 
+// The last few plans of this thread, keyed by every input of the planner (the plan is a
+// pure function of them), so that a repeated call skips the cost model.
+struct PlanKey {
+    int64_t m, ws_bytes;
+    int layout, n, k, num_groups, expected_m, scale_mode, form, cus, forced, splits;
+    bool operator==(const PlanKey& o) const {
+        return m == o.m && ws_bytes == o.ws_bytes && layout == o.layout && n == o.n &&
+               k == o.k && num_groups == o.num_groups && expected_m == o.expected_m &&
+               scale_mode == o.scale_mode && form == o.form && cus == o.cus &&
+               forced == o.forced && splits == o.splits;
+    }
+};
+struct PlanCacheEntry {
+    bool valid;
+    PlanKey key;
+    fp8bs::Plan plan;
+};
+constexpr int kPlanCacheEntries = 8;
+thread_local PlanCacheEntry t_plans[kPlanCacheEntries];
+thread_local int t_plan_next = 0;
+
 // Plan for a request on the current device, honouring the test pins.
 int make_plan(int layout, int64_t m, int n, int k, int num_groups, int expected_m,
               int64_t ws_bytes, int* cus_out, fp8bs::Plan* pl, int scale_mode = fp8bs::kScaleF32,
@@ -74,14 +95,29 @@ int make_plan(int layout, int64_t m, int n, int k, int num_groups, int expected_
     const int cus = current_num_cus();
     if (cus <= 0) return FP8BS_ERR_HIP;
     *cus_out = cus;
+    const int forced = g_forced_instance.load(std::memory_order_relaxed);
+    const int splits = ws_bytes > 0 ? g_forced_splits.load(std::memory_order_relaxed) : 1;
+    const PlanKey key{m, ws_bytes, layout, n, k, num_groups, expected_m, scale_mode, form, cus,
+                      forced, splits};
+    for (const PlanCacheEntry& e : t_plans) {
+        if (e.valid && e.key == key) {
+            *pl = e.plan;
+            return FP8BS_OK;
+        }
+    }
     int st = fp8bs::plan_request(layout, m, n, k, num_groups, expected_m, cus, ws_bytes, pl,
                                  scale_mode, form);
     if (st != FP8BS_OK) return st;
-    const int forced = g_forced_instance.load(std::memory_order_relaxed);
-    const int splits = ws_bytes > 0 ? g_forced_splits.load(std::memory_order_relaxed) : 1;
     if (forced >= 0 || splits > 0)
         st = fp8bs::plan_instance(forced >= 0 ? forced : pl->instance, splits, layout, m, n, k,
                                   num_groups, expected_m, cus, ws_bytes, pl, scale_mode, form);
+    if (st == FP8BS_OK) {
+        PlanCacheEntry& e = t_plans[t_plan_next];
+        t_plan_next = (t_plan_next + 1) % kPlanCacheEntries;
+        e.valid = true;
+        e.key = key;
+        e.plan = *pl;
+    }
     return st;
 }
 
