@@ -44,7 +44,10 @@
  *     must stay alive until the stream work completes.
  *   - Inputs are read-only.  D is written only at valid rows (see each call)
  *     and columns n < N; every other byte of D is left untouched.
- *   - Pointers must be 16-byte aligned.  K must be a positive multiple of 128.
+ *   - Pointers must be 16-byte aligned.  A call with no output rows (m, m_total
+ *     or max_m == 0) checks its sizes, then returns FP8BS_OK without launching
+ *     and without looking at any pointer (an empty buffer may be NULL).
+ *     K must be a positive multiple of 128.
  *     One A slot (rows x K bytes: m, m_total or max_m rows) and one B group
  *     (N x K bytes) must each be smaller than 4 GiB.
  *   - SFA is stored MN-major ("transposed"): element (row r, K group c) lives at

@@ -139,6 +139,9 @@ int run(int layout, const void* a, const float* sfa, const void* b, const float*
         }
         if (total != k) return FP8BS_ERR_SHAPE;
     }
+    // No output rows: nothing is launched and no pointer is dereferenced, so none is
+    // checked (an empty torch tensor, say a batch routed to no expert, has a NULL pointer).
+    if (m == 0) return FP8BS_OK;
     // (a K-grouped call with k_total == 0 reads no operand: those pointers may be NULL)
     const bool operands_read = !(kg && k == 0);
     if (operands_read &&
@@ -148,7 +151,6 @@ int run(int layout, const void* a, const float* sfa, const void* b, const float*
     if (layout != fp8bs::kDense && !kg && !aligned4(group_data)) return FP8BS_ERR_POINTER;
     if (ws_bytes > 0 && !aligned16(ws)) return FP8BS_ERR_POINTER;
     if (want_c && !aligned16(c)) return FP8BS_ERR_POINTER;
-    if (m == 0) return FP8BS_OK;
     const int64_t ws_cap = ws_bytes > (size_t)INT64_MAX ? INT64_MAX : (int64_t)ws_bytes;
     int cus = 0;
     fp8bs::Plan pl;

@@ -135,6 +135,39 @@ def test_entry_points_validate_before_launching():
     assert lib.fp8bs_grouped_masked_nt(f, f, f, f, f, f, 2, 0, 0, 16, 128, None) == OK
 
 
+
+def test_empty_calls_need_no_pointers():
+    """No output rows: the sizes are still checked, then OK with every buffer NULL (an
+    empty torch tensor has a NULL data pointer)."""
+    lib = fp8bs._load()
+    N = None
+    assert lib.fp8bs_dense_nt(N, N, N, N, N, 0, 16, 128, N) == OK
+    assert lib.fp8bs_dense_nt(N, N, N, N, N, 0, 16, 100, N) == ERR_SHAPE
+    assert lib.fp8bs_dense_nt_ws(N, N, N, N, N, 0, 16, 128, N, 0, N) == OK
+    assert lib.fp8bs_dense_nt_c(N, N, N, N, N, N, 0, 16, 128, N, 0, N) == OK
+    assert lib.fp8bs_dense_nt_ue8m0(N, N, N, N, N, 0, 16, 128, N, 0, N) == OK
+    for form in ("nn", "tn", "tt"):
+        assert getattr(lib, "fp8bs_dense_" + form)(N, N, N, N, N, N, 0, 16, 128, N, 0, N) == OK
+        assert getattr(lib, f"fp8bs_dense_{form}_ue8m0")(N, N, N, N, N, N, 0, 16, 128, N, 0,
+                                                         N) == OK
+    assert lib.fp8bs_grouped_contiguous_nt(N, N, N, N, N, N, 0, 16, 128, 2, N) == OK
+    assert lib.fp8bs_grouped_contiguous_nt(N, N, N, N, N, N, 0, 16, 128, 0, N) == ERR_SHAPE
+    assert lib.fp8bs_grouped_contiguous_nt_ws(N, N, N, N, N, N, 0, 16, 128, 2, N, 0, N) == OK
+    assert lib.fp8bs_grouped_contiguous_nt_c(N, N, N, N, N, N, N, 0, 16, 128, 2, N, 0, N) == OK
+    assert lib.fp8bs_grouped_contiguous_nt_ue8m0(N, N, N, N, N, N, 0, 16, 128, 2, N, 0, N) == OK
+    assert lib.fp8bs_grouped_masked_nt(N, N, N, N, N, N, 2, 0, 0, 16, 128, N) == OK
+    assert lib.fp8bs_grouped_masked_nt_c(N, N, N, N, N, N, N, 2, 0, 0, 16, 128, N, 0, N) == OK
+    assert lib.fp8bs_grouped_masked_nt_ue8m0(N, N, N, N, N, N, 2, 0, 0, 16, 128, N, 0, N) == OK
+    # K-grouped: m >= 16 always; its empty call is k_total == 0 (D = C or zeros), which
+    # reads no operand but still needs d and the host-side group sizes
+    ks = (ctypes.c_int32 * 2)(0, 0)
+    assert lib.fp8bs_k_grouped_tn_contiguous(N, N, N, N, N, N, ks, 2, 0, 16, 0, N, 0, N) \
+        == ERR_SHAPE
+    assert lib.fp8bs_k_grouped_tn_contiguous(N, N, N, N, N, N, N, 2, 16, 16, 0, N, 0, N) \
+        == ERR_POINTER
+    assert lib.fp8bs_k_grouped_tn_contiguous(N, N, N, N, N, N, ks, 2, 16, 16, 0, N, 0, N) \
+        == ERR_POINTER
+
 def test_cu_cap_and_forced_instance_setters():
     prev = fp8bs.set_num_cus(100)
     try:

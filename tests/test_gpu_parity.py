@@ -13,7 +13,7 @@ import torch
 import moe_grouped_gemm_block_amd as fp8bs
 from moe_grouped_gemm_block_amd import synth
 from _helpers import (SENTINEL, DeviceProblem, check_full, check_values, oracle_full,
-                      bf16_bits_to_f64)
+                      bf16_bits_to_f64, out_shape)
 
 pytestmark = pytest.mark.gpu
 
@@ -306,3 +306,25 @@ def test_zero_rows_is_a_no_op():
     assert fp8bs._load().fp8bs_grouped_masked_nt(ptr, ptr, ptr, ptr, ptr, ptr, 2, 0, 0, 16, 128,
                                                  None) == 0
     torch.cuda.synchronize()
+
+
+def test_empty_torch_tensors_are_a_no_op():
+    """No output rows through the binding: zero-row tensors have NULL data pointers, and
+    every entry point takes the call as done (nothing launched, nothing written)."""
+    cases = [synth.make_dense(0, 64, 256, seed=11),
+             synth.make_contiguous(2, 64, 256, seed=12, counts=[0, 0]),
+             synth.make_masked(2, 0, 64, 256, seed=13, masked_m=[0, 0])]
+    for p in cases:
+        print(f"[gpu] empty {p.kind} M={p.M}", flush=True)
+        dp = DeviceProblem(p)
+        dp.run(workspace=True)
+        dp.run(workspace=False)
+        c = torch.zeros(out_shape(p), dtype=torch.float32, device="cuda")
+        if p.kind == "dense":
+            fp8bs.fp8bs_dense_nt_c(dp.a, dp.sfa, dp.b, dp.sfb, c, dp.d)
+        elif p.kind == "contiguous":
+            fp8bs.fp8bs_grouped_contiguous_nt_c(dp.a, dp.sfa, dp.b, dp.sfb, c, dp.d, dp.layout)
+        else:
+            fp8bs.fp8bs_grouped_masked_nt_c(dp.a, dp.sfa, dp.b, dp.sfb, c, dp.d, dp.masked_m)
+        torch.cuda.synchronize()
+        assert dp.d.numel() == 0 or bool((dp.d == SENTINEL).all())
