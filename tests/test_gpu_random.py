@@ -1,8 +1,10 @@
 """Seeded random parity cases: entry point (workspace or not, FP32 addend, packed UE8M0
 scales, the nn / tn / tt stored forms), layout, sizes (ragged and odd, down to one row or
 column), instance (forced or the planner's) and K split drawn at random, each checked
-against the oracle over the whole output (valid rows to tolerance, the rest untouched).
-Every case is fixed by the seed, so a failure names a reproducible case."""
+against the oracle over the whole output (valid rows to tolerance, the rest untouched);
+and the same for the K-grouped weight-gradient call (group sizes with empty groups, FP32
+addend in place or apart, UE8M0 scales, split K).  Every case is fixed by the seed, so a
+failure names a reproducible case."""
 import numpy as np
 import pytest
 import torch
@@ -11,6 +13,7 @@ import moe_grouped_gemm_block_amd as fp8bs
 from moe_grouped_gemm_block_amd import synth
 from _helpers import DeviceProblem, check_full, oracle_full
 import test_gpu_addend as addend_t
+import test_gpu_kgrouped as kg_t
 import test_gpu_layouts as layouts_t
 import test_gpu_ue8m0 as ue8m0_t
 
@@ -87,3 +90,41 @@ def test_random_case(i):
         dp = DeviceProblem(p)
         dp.run(workspace=variant == "ws")
         check_full(p, dp.result(), oracle_full(p), what)
+
+
+N_KG_CASES = 40
+
+
+def _kg_case(i):
+    rng = np.random.default_rng(SEED + 1000 + i)
+    variant = str(rng.choice(["plain", "addend", "in_place", "ue8m0", "split"]))
+    G = int(rng.integers(1, 9))
+    M = 16 * int(rng.integers(1, 25))
+    N = 16 * int(rng.integers(1, 25))
+    counts = [int(c) if rng.random() > 0.25 else 0 for c in rng.integers(1, 700, size=G)]
+    p = synth.make_k_grouped(G, M, N, seed=SEED + 1000 + i, counts=counts,
+                             pow2=variant == "ue8m0")
+    pool = kg_t.E8_MN_INSTANCES if variant == "ue8m0" else kg_t.MN_INSTANCES
+    inst = int(rng.choice(pool)) if rng.random() < 0.7 else -1
+    splits = int(rng.choice([2, 3, 5])) if variant == "split" else 0
+    if splits:                                  # a pinned count the call can use
+        splits = max(1, min(splits, int(sum(p.ks)) // 128))
+    C = None
+    if variant in ("addend", "in_place") or rng.random() < 0.3:
+        C = (rng.standard_normal((G, M, N)) * 4).astype(np.float32)
+    return p, variant, inst, splits, C
+
+
+@pytest.mark.parametrize("i", range(N_KG_CASES))
+def test_random_k_grouped_case(i):
+    p, variant, inst, splits, C = _kg_case(i)
+    what = (f"k-grouped case {i}: {variant} G={p.G} M={p.M} N={p.N} ks={list(p.ks)} "
+            f"inst={inst} splits={splits} addend={C is not None}")
+    print(f"[gpu] {what}", flush=True)
+    fp8bs.force_instance(inst)
+    fp8bs.force_splits(splits)
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+    if variant == "ue8m0":
+        kg_t._full_e8(p, what, C=C, workspace=ws)
+    else:
+        kg_t._full(p, what, C=C, workspace=ws, in_place=variant == "in_place")
