@@ -402,24 +402,41 @@ def ingest_traffic(fetch_dir, write_dir, name):
 
 
 def summarize_trace(d, family):
-    """Average duration per workload shape from a kernel trace of `bench.py --family F`:
-    the GEMM dispatches cycle through the family's shapes in order."""
+    """Average duration per workload shape from a kernel trace of `bench.py --family F`.
+    Each call is one GEMM dispatch (staged or B-streaming kernel), followed by a split-K
+    reduction when its plan splits K; the calls cycle through the family's shapes in
+    order, so a GEMM dispatch starts the next shape and a reduction belongs to the GEMM
+    before it."""
     import csv
     import glob
     from moe_grouped_gemm_block_amd import synth
     names = [x["name"] for x in synth.workload_shapes(family)]
+    kinds = ("fp8bs_gemm_kernel", "fp8bs_stream_kernel", "fp8bs_splitk_reduce")
     rows = []
     for path in glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True):
-        rows += [r for r in csv.DictReader(open(path)) if "fp8bs_gemm_kernel" in r["Kernel_Name"]]
+        rows += [r for r in csv.DictReader(open(path))
+                 if any(k in r["Kernel_Name"] for k in kinds)]
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
-    per = {n: [] for n in names}
-    for i, r in enumerate(rows):
-        per[names[i % len(names)]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    gemm = {n: [] for n in names}
+    red = {n: [] for n in names}
+    call = -1
+    for r in rows:
+        us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        if "fp8bs_splitk_reduce" in r["Kernel_Name"]:
+            if call >= 0:
+                red[names[call % len(names)]].append(us)
+        else:
+            call += 1
+            gemm[names[call % len(names)]].append(us)
     out = {}
     for n in names:
-        v = per[n]
-        out[n] = {"dispatches": len(v), "avg_us": sum(v) / max(1, len(v)),
-                  "min_us": min(v) if v else None, "max_us": max(v) if v else None}
+        v, w = gemm[n], red[n]
+        avg = sum(v) / max(1, len(v))
+        ravg = sum(w) / len(w) if w else 0.0
+        out[n] = {"dispatches": len(v), "avg_us": avg,
+                  "min_us": min(v) if v else None, "max_us": max(v) if v else None,
+                  "reduce_dispatches": len(w), "reduce_avg_us": ravg,
+                  "call_avg_us": avg + (ravg * len(w) / len(v) if v else 0.0)}
     print(json.dumps(out, indent=1))
 
 

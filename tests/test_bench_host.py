@@ -47,3 +47,39 @@ def test_traffic_absent_or_unreadable(tmp_path, monkeypatch):
     assert bench.load_traffic("shape_a") is None
     (tmp_path / "profiles" / "traffic.json").write_text("{not json")
     assert bench.load_traffic("shape_a") is None
+
+
+def test_trace_summary_charges_reductions_to_their_call(tmp_path, capsys):
+    """A kernel trace of two steps of the decode family: each call is one GEMM dispatch
+    (staged or B-streaming), some followed by a split-K reduction; other kernels are
+    ignored."""
+    from moe_grouped_gemm_block_amd import synth
+    names = [x["name"] for x in synth.workload_shapes(2)]
+    lines = ["Kernel_Name,Start_Timestamp,End_Timestamp"]
+    t = 0
+    expect_gemm = {n: [] for n in names}
+    expect_red = {n: [] for n in names}
+    for step in range(2):
+        for i, n in enumerate(names):
+            kind = "fp8bs_stream_kernel<64>" if i % 2 else "fp8bs_gemm_kernel<256>"
+            dur = 1000 * (i + 1) + step * 10
+            lines.append(f"\"{kind}\",{t},{t + dur}")
+            expect_gemm[n].append(dur / 1e3)
+            t += dur + 50
+            lines.append(f"\"spin_kernel\",{t},{t + 7}")
+            t += 100
+            if i % 3 == 0:
+                lines.append(f"\"fp8bs_splitk_reduce<64>\",{t},{t + 300 + i}")
+                expect_red[n].append((300 + i) / 1e3)
+                t += 400
+    (tmp_path / "run").mkdir()
+    (tmp_path / "run" / "kt_kernel_trace.csv").write_text("\n".join(lines) + "\n")
+    bench.summarize_trace(str(tmp_path), 2)
+    out = json.loads(capsys.readouterr().out)
+    for n in names:
+        g, r = expect_gemm[n], expect_red[n]
+        assert out[n]["dispatches"] == 2
+        assert abs(out[n]["avg_us"] - sum(g) / 2) < 1e-9
+        assert out[n]["reduce_dispatches"] == len(r)
+        ravg = sum(r) / len(r) if r else 0.0
+        assert abs(out[n]["call_avg_us"] - (sum(g) / 2 + ravg * len(r) / 2)) < 1e-9
