@@ -78,7 +78,7 @@ int64_t split_workspace_bytes(const InstanceShape& shape, int64_t tiles, int spl
 // written once and read once); a split launch adds the reduction kernel; and a launch
 // that leaves CUs idle keeps fewer loads in flight, so under-fill is penalised.
 static const double kHbmBytesPerNs = 8.0e12 / 1.0e9;
-static const double kReduceFixedNs = 1500.0;         // second launch and its tail
+static const double kReduceFixedNs = 4300.0;         // second launch: 4.2-4.8 us traced
 static const double kReduceBytesPerNs = 4.0e12 / 1.0e9;
 static const int kMaxSplits = 16;
 static const double kRidgeFlopPerByte = 629.0;       // dense FP8 MFMA peak / HBM bandwidth
