@@ -1,0 +1,55 @@
+"""Calls from several host threads at once: each thread plans and launches its own layouts
+on its own stream, repeatedly, while the others do the same.  The library keeps its plan
+cache per thread and takes no lock, so every result must still match the oracle."""
+import threading
+
+import numpy as np
+import pytest
+import torch
+
+import moe_grouped_gemm_block_amd as fp8bs
+from moe_grouped_gemm_block_amd import synth
+from _helpers import DeviceProblem, check_full, oracle_full
+
+pytestmark = pytest.mark.gpu
+
+ROUNDS = 6
+
+
+def _problems(t):
+    return [synth.make_dense(200 + 17 * t, 300 + 16 * t, 512, seed=3000 + t),
+            synth.make_contiguous(3, 256, 384, seed=3100 + t, counts=[70 + t, 0, 150]),
+            synth.make_masked(4, 96, 208, 256, seed=3200 + t, masked_m=[5, 96, 0, 40 + t])]
+
+
+def test_threads_with_their_own_streams():
+    n_threads = 4
+    # inputs and oracle results prepared up front (the oracle is CPU work)
+    cases = [[(p, oracle_full(p)) for p in _problems(t)] for t in range(n_threads)]
+    errors = []
+
+    def worker(t):
+        try:
+            stream = torch.cuda.Stream()
+            dps = [DeviceProblem(p) for p, _ in cases[t]]
+            torch.cuda.current_stream().synchronize()     # uploads done before use
+            for r in range(ROUNDS):
+                with torch.cuda.stream(stream):
+                    for dp in dps:
+                        dp.reset()
+                        dp.run(stream=stream, workspace=(r + t) % 2 == 0)
+                stream.synchronize()
+                for dp, (p, ref) in zip(dps, cases[t]):
+                    check_full(p, dp.d.cpu().numpy().view(np.uint16), ref,
+                               f"thread {t} round {r} {p.kind}")
+        except BaseException as e:                     # reported by the main thread
+            errors.append((t, e))
+
+    print(f"[gpu] {n_threads} threads x {ROUNDS} rounds x 3 layouts", flush=True)
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(n_threads)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join(timeout=100)
+    assert not any(th.is_alive() for th in threads), "a thread did not finish"
+    assert not errors, errors[0]
