@@ -312,11 +312,32 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const Tile& tl, 
         lo = pack_bf16x2(v[0], v[1]);
         hi = pack_bf16x2(v[2], v[3]);
     };
+    // Contiguous: which of this wavefront's rows hold the tile's expert, found before any
+    // store (a load between the stores would wait for every earlier store of the
+    // wavefront: the memory counter retires in issue order).  Each lane reads one row of
+    // each 64-row half of the wavefront's rows and a ballot turns the answers into a
+    // 64-bit mask per half; the lane's own rows lie in one half.
+    uint64_t expert_rows = 0;
+    int expert_bit0 = 0;
+    if constexpr (LAYOUT == kContiguous) {
+        static_assert(!ROWS16 && WTM <= 128, "row masks cover two 64-row halves");
+        uint64_t half[2] = {0, 0};
+#pragma unroll
+        for (int h = 0; h < (WTM + 63) / 64; ++h) {
+            const int r = tl.m0 + wm * WTM + 64 * h + lj + 16 * kq;
+            const bool mine = r < tl.row_limit &&
+                              p.grouped_layout[min(r, tl.row_limit - 1)] == tl.g;
+            half[h] = __ballot(mine);
+        }
+        expert_rows = (TM * lj) < 64 ? half[0] : half[1];
+        expert_bit0 = (TM * lj) & 63;
+    }
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
         const int row = tl.m0 + wm * WTM + (ROWS16 ? 16 * i + lj : TM * lj + (i ^ flip));
         bool ok = row < tl.row_limit;
-        if (LAYOUT == kContiguous && ok) ok = p.grouped_layout[row] == tl.g;
+        if constexpr (LAYOUT == kContiguous)
+            ok = ok && ((expert_rows >> (expert_bit0 + (i ^ flip))) & 1u);
         uint16_t* drow = d_g + (int64_t)row * p.n;
         const float* crow = (p.c && ok) ? p.c + slot + (int64_t)row * p.n : nullptr;
         // Four column blocks at a time: the four lanes of a row (quarters kq = 0..3) hold
