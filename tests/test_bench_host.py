@@ -52,34 +52,58 @@ def test_traffic_absent_or_unreadable(tmp_path, monkeypatch):
 def test_trace_summary_charges_reductions_to_their_call(tmp_path, capsys):
     """A kernel trace of two steps of the decode family: each call is one GEMM dispatch
     (staged or B-streaming), some followed by a split-K reduction; other kernels are
-    ignored."""
+    ignored.  The first step's calls follow a fill kernel (the cache flush): cold; the
+    second step's do not: warm."""
     from moe_grouped_gemm_block_amd import synth
     names = [x["name"] for x in synth.workload_shapes(2)]
     lines = ["Kernel_Name,Start_Timestamp,End_Timestamp"]
     t = 0
-    expect_gemm = {n: [] for n in names}
-    expect_red = {n: [] for n in names}
+    expect = {k: ({n: [] for n in names}, {n: [] for n in names}) for k in ("cold", "warm")}
     for step in range(2):
+        kind_t = "cold" if step == 0 else "warm"
         for i, n in enumerate(names):
+            if step == 0:
+                lines.append(f"\"vectorized_elementwise_kernel<FillFunctor<int> >\",{t},{t + 90}")
+                t += 100
             kind = "fp8bs_stream_kernel<64>" if i % 2 else "fp8bs_gemm_kernel<256>"
             dur = 1000 * (i + 1) + step * 10
             lines.append(f"\"{kind}\",{t},{t + dur}")
-            expect_gemm[n].append(dur / 1e3)
+            expect[kind_t][0][n].append(dur / 1e3)
             t += dur + 50
             lines.append(f"\"spin_kernel\",{t},{t + 7}")
             t += 100
             if i % 3 == 0:
                 lines.append(f"\"fp8bs_splitk_reduce<64>\",{t},{t + 300 + i}")
-                expect_red[n].append((300 + i) / 1e3)
+                expect[kind_t][1][n].append((300 + i) / 1e3)
                 t += 400
     (tmp_path / "run").mkdir()
     (tmp_path / "run" / "kt_kernel_trace.csv").write_text("\n".join(lines) + "\n")
     bench.summarize_trace(str(tmp_path), 2)
     out = json.loads(capsys.readouterr().out)
-    for n in names:
-        g, r = expect_gemm[n], expect_red[n]
-        assert out[n]["dispatches"] == 2
-        assert abs(out[n]["avg_us"] - sum(g) / 2) < 1e-9
-        assert out[n]["reduce_dispatches"] == len(r)
-        ravg = sum(r) / len(r) if r else 0.0
-        assert abs(out[n]["call_avg_us"] - (sum(g) / 2 + ravg * len(r) / 2)) < 1e-9
+    for kind_t in ("cold", "warm"):
+        for n in names:
+            g, r = expect[kind_t][0][n], expect[kind_t][1][n]
+            rec = out[n][kind_t]
+            assert rec["dispatches"] == 1
+            assert abs(rec["avg_us"] - sum(g)) < 1e-9
+            assert rec["reduce_dispatches"] == len(r)
+            ravg = sum(r) / len(r) if r else 0.0
+            assert abs(rec["call_avg_us"] - (sum(g) + ravg * len(r))) < 1e-9
+
+
+def test_family_list_and_cpu_model():
+    assert bench.parse_families("none", 3) == []
+    assert bench.parse_families("0,1,3,2,1", 3) == [0, 1, 2]
+    with pytest.raises(SystemExit):
+        bench.parse_families("9", 3)
+    assert isinstance(bench.cpu_model(), str) and bench.cpu_model()
+
+
+def test_input_hash_covers_group_data():
+    from moe_grouped_gemm_block_amd import synth
+    p = synth.make_contiguous(2, 64, 128, seed=5, total_rows=200)
+    h = bench.input_sha256(p)
+    assert h == bench.input_sha256(p)
+    p.layout = p.layout.copy()
+    p.layout[0] = -1
+    assert bench.input_sha256(p) != h
