@@ -56,8 +56,9 @@
  *   - Errors are reported by the return value before anything is launched;
  *     nothing is printed (unless FP8BS_PRINT_CONFIGS=1) and nothing aborts.
  *     A launch failure reported by the HIP runtime maps to FP8BS_ERR_HIP.
- *   - Thread-safe.  The only global state is the CU cap (fp8bs_set_num_cus)
- *     and the test pins (fp8bs_force_instance, fp8bs_force_splits).
+ *   - Thread-safe.  The only process-wide state is the CU cap
+ *     (fp8bs_set_num_cus); the test pins (fp8bs_force_instance,
+ *     fp8bs_force_splits) and the plan cache belong to the calling thread.
  *   - Graph-capturable: device-side group data (grouped_layout, masked_m) is
  *     never read on the host.
  */
@@ -86,7 +87,9 @@ typedef enum {
 /* Layout codes for the planner queries (fp8bs_plan_query, fp8bs_workspace_size,
  * fp8bs_count_tiles, fp8bs_describe_config).  The first three are the NT entry
  * points; K_GROUPED is fp8bs_k_grouped_tn_contiguous (m = M, k = K_total, num_groups
- * groups); DENSE_NN / _TN / _TT are fp8bs_dense_nn / _tn / _tt. */
+ * groups); DENSE_NN / _TN / _TT are fp8bs_dense_nn / _tn / _tt.  OR-ing
+ * FP8BS_LAYOUT_UE8M0 into a code asks about the packed power-of-two (_ue8m0) call of
+ * that layout, which can only run the instances compiled for those scales. */
 typedef enum {
     FP8BS_LAYOUT_DENSE = 0,
     FP8BS_LAYOUT_CONTIGUOUS = 1,
@@ -94,7 +97,8 @@ typedef enum {
     FP8BS_LAYOUT_K_GROUPED = 3,
     FP8BS_LAYOUT_DENSE_NN = 4,
     FP8BS_LAYOUT_DENSE_TN = 5,
-    FP8BS_LAYOUT_DENSE_TT = 6
+    FP8BS_LAYOUT_DENSE_TT = 6,
+    FP8BS_LAYOUT_UE8M0 = 16
 } fp8bs_layout;
 
 /*
@@ -375,14 +379,15 @@ int fp8bs_set_num_cus(int n);
 /* The current cap (0 = no cap). */
 int fp8bs_get_num_cus(void);
 
-/* Pins every later call to compiled instance i (see fp8bs_instance_info);
- * -1 restores the planner's choice.  For testing and measuring tile shapes:
+/* Pins every later call of the calling thread to compiled instance i (see
+ * fp8bs_instance_info); -1 restores the planner's choice.  Other threads' calls are
+ * not affected.  For testing and measuring tile shapes:
  * the choice of instance changes speed, never results.  Returns the previous
  * setting, or -2 for an index out of range. */
 int fp8bs_force_instance(int i);
 
-/* Pins the K split count of later _ws calls to s >= 1 (1 = no split); 0
- * restores the planner's choice.  A pinned count that the request cannot use
+/* Pins the K split count of the calling thread's later _ws calls to s >= 1 (1 = no
+ * split); 0 restores the planner's choice.  A pinned count that the request cannot use
  * (s > K/128, or more workspace than lent) makes the call fail with
  * FP8BS_ERR_UNSUPPORTED.  For testing and measuring; changes speed, and
  * results only within the bound stated for the _ws calls.  Returns the previous

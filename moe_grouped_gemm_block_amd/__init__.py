@@ -36,11 +36,12 @@ __all__ = [
     "fp8bs_dense_nn_ue8m0", "fp8bs_dense_tn_ue8m0", "fp8bs_dense_tt_ue8m0",
     "fp8bs_k_grouped_tn_contiguous_ue8m0",
     "LAYOUT_DENSE", "LAYOUT_CONTIGUOUS", "LAYOUT_MASKED", "LAYOUT_K_GROUPED",
-    "LAYOUT_DENSE_NN", "LAYOUT_DENSE_TN", "LAYOUT_DENSE_TT",
+    "LAYOUT_DENSE_NN", "LAYOUT_DENSE_TN", "LAYOUT_DENSE_TT", "LAYOUT_UE8M0",
 ]
 
 LAYOUT_DENSE, LAYOUT_CONTIGUOUS, LAYOUT_MASKED = 0, 1, 2
 LAYOUT_K_GROUPED, LAYOUT_DENSE_NN, LAYOUT_DENSE_TN, LAYOUT_DENSE_TT = 3, 4, 5, 6
+LAYOUT_UE8M0 = 16                 # OR-ed into a layout code: the packed power-of-two calls
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "lib", "libfp8bs.so")
@@ -187,7 +188,8 @@ def instances() -> list:
 
 
 def force_instance(i: int) -> int:
-    """Pin every later call to compiled instance i (-1 = planner's choice); returns the previous."""
+    """Pin every later call of this thread to compiled instance i (-1 = planner's choice);
+    returns the previous."""
     prev = int(_load().fp8bs_force_instance(int(i)))
     if prev == -2:
         raise ValueError(f"no compiled instance {i}")
@@ -195,7 +197,8 @@ def force_instance(i: int) -> int:
 
 
 def force_splits(s: int) -> int:
-    """Pin the K split count of later workspace calls (0 = planner's choice); returns the previous."""
+    """Pin the K split count of this thread's later workspace calls (0 = planner's choice);
+    returns the previous."""
     prev = int(_load().fp8bs_force_splits(int(s)))
     if prev == -1:
         raise ValueError(f"invalid split count {s}")
@@ -711,7 +714,8 @@ def _dense_form(form, a, sfa, b, sfb, c, d, workspace, stream, e8=False):
     name = "fp8bs_dense_" + form + ("_ue8m0" if e8 else "")
     with _on_device(a):
         s = stream
-        wp, wb, _keep = _workspace(workspace, code, m, n, k, 1, 0, s, a.device)
+        wp, wb, _keep = _workspace(workspace, code | (LAYOUT_UE8M0 if e8 else 0), m, n, k, 1, 0,
+                                   s, a.device)
         st = getattr(_load(), name)(*args, cp, dp, m, n, k, wp, wb, _stream_handle(s, a.device))
     _check(st, name)
 
@@ -788,7 +792,8 @@ def _k_grouped(a, sfa, b, sfb, d, ks, c, workspace, stream, e8):
     ks_host = (ctypes.c_int32 * max(g, 1))(*sizes)
     with _on_device(a):
         s = stream
-        wp, wb, _keep = _workspace(workspace, LAYOUT_K_GROUPED, m, n, k_total, g, 0, s, a.device)
+        wp, wb, _keep = _workspace(workspace, LAYOUT_K_GROUPED | (LAYOUT_UE8M0 if e8 else 0), m,
+                                   n, k_total, g, 0, s, a.device)
         name = "fp8bs_k_grouped_tn_contiguous" + ("_ue8m0" if e8 else "")
         st = getattr(_load(), name)(*args, cp, dp, ks_host, g, m, n, k_total, wp, wb,
                                     _stream_handle(s, a.device))

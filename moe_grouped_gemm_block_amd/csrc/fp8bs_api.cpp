@@ -14,8 +14,9 @@
 namespace {
 
 std::atomic<int> g_cu_cap{0};
-std::atomic<int> g_forced_instance{-1};
-std::atomic<int> g_forced_splits{0};
+// Test pins: per thread, so that one thread's pin never changes another thread's calls.
+thread_local int t_forced_instance = -1;
+thread_local int t_forced_splits = 0;
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_dev_cus[kMaxDevices];   // 0 = not queried yet
 
@@ -52,14 +53,16 @@ int layout_code(int layout, int form) {
 }
 
 void format_plan(const fp8bs::Plan& pl, int layout, int form, int64_t m, int n, int k, int g,
-                 int expected_m, int cus, char* buf, size_t len) {
+                 int expected_m, int cus, char* buf, size_t len,
+                 int scale_mode = fp8bs::kScaleF32) {
     static const char* names[7] = {"dense", "contiguous", "masked", "k-grouped tn",
                                    "dense nn", "dense tn", "dense tt"};
     snprintf(buf, len,
-             "fp8bs %s m=%lld n=%d k=%d groups=%d expected_m=%d cus=%d -> %s block %dx%d "
+             "fp8bs %s%s m=%lld n=%d k=%d groups=%d expected_m=%d cus=%d -> %s block %dx%d "
              "waves %dx%d threads %d stages %d lds %dB wg/cu %d tiles %lld splits %d "
              "workspace %lldB grid %lld raster %d instance %d",
-             names[layout_code(layout, form)], (long long)m, n, k, g, expected_m, cus,
+             names[layout_code(layout, form)], scale_mode == fp8bs::kScaleUE8M0 ? " ue8m0" : "",
+             (long long)m, n, k, g, expected_m, cus,
              pl.shape.kind == fp8bs::kStreamB ? "stream-B" : "staged", pl.shape.block_m,
              pl.shape.block_n, pl.shape.waves_m, pl.shape.waves_n,
              64 * pl.shape.waves_m * pl.shape.waves_n, pl.shape.stages, pl.shape.lds_bytes,
@@ -95,8 +98,8 @@ int make_plan(int layout, int64_t m, int n, int k, int num_groups, int expected_
     const int cus = current_num_cus();
     if (cus <= 0) return FP8BS_ERR_HIP;
     *cus_out = cus;
-    const int forced = g_forced_instance.load(std::memory_order_relaxed);
-    const int splits = ws_bytes > 0 ? g_forced_splits.load(std::memory_order_relaxed) : 1;
+    const int forced = t_forced_instance;
+    const int splits = ws_bytes > 0 ? t_forced_splits : 1;
     const PlanKey key{m, ws_bytes, layout, n, k, num_groups, expected_m, scale_mode, form, cus,
                       forced, splits};
     for (const PlanCacheEntry& e : t_plans) {
@@ -158,7 +161,8 @@ int run(int layout, const void* a, const float* sfa, const void* b, const float*
     if (st != FP8BS_OK) return st;
     if (print_configs()) {
         char line[512];
-        format_plan(pl, layout, form, m, n, k, num_groups, expected_m, cus, line, sizeof line);
+        format_plan(pl, layout, form, m, n, k, num_groups, expected_m, cus, line, sizeof line,
+                    scale_mode);
         fprintf(stderr, "%s\n", line);
     }
     fp8bs::GemmParams p;
@@ -358,8 +362,9 @@ int fp8bs_k_grouped_tn_contiguous_ue8m0(const void* a, const int32_t* sfa, const
 
 int64_t fp8bs_workspace_size(int layout_code, int64_t m, int n, int k, int num_groups,
                              int expected_m) {
-    int layout, form;
-    if (!fp8bs::decode_layout(layout_code, &layout, &form)) return -FP8BS_ERR_UNSUPPORTED;
+    int layout, form, scale_mode;
+    if (!fp8bs::decode_layout(layout_code, &layout, &form, &scale_mode))
+        return -FP8BS_ERR_UNSUPPORTED;
     const int g = layout == fp8bs::kDense ? 1 : num_groups;
     int st = fp8bs::validate_sizes(layout, m, n, k, g, form);
     if (st != FP8BS_OK) return -st;
@@ -367,7 +372,7 @@ int64_t fp8bs_workspace_size(int layout_code, int64_t m, int n, int k, int num_g
     int cus = 0;
     fp8bs::Plan pl;
     // the planner's choice with unlimited workspace, then any pins
-    st = make_plan(layout, m, n, k, g, expected_m, INT64_MAX, &cus, &pl, fp8bs::kScaleF32, form);
+    st = make_plan(layout, m, n, k, g, expected_m, INT64_MAX, &cus, &pl, scale_mode, form);
     if (st != FP8BS_OK) return -st;
     return pl.workspace_bytes;
 }
@@ -381,29 +386,34 @@ int fp8bs_get_num_cus(void) { return g_cu_cap.load(); }
 
 int fp8bs_force_instance(int i) {
     if (i < -1 || i >= fp8bs::kNumInstances) return -2;
-    return g_forced_instance.exchange(i);
+    const int prev = t_forced_instance;
+    t_forced_instance = i;
+    return prev;
 }
 
 int fp8bs_force_splits(int s) {
     if (s < 0) return -1;
-    return g_forced_splits.exchange(s);
+    const int prev = t_forced_splits;
+    t_forced_splits = s;
+    return prev;
 }
 
 int fp8bs_describe_config(int layout_code, int64_t m, int n, int k, int num_groups,
                           int expected_m, char* buf, size_t len) {
     if (!buf || len == 0) return FP8BS_ERR_POINTER;
-    int layout, form;
-    if (!fp8bs::decode_layout(layout_code, &layout, &form)) return FP8BS_ERR_UNSUPPORTED;
+    int layout, form, scale_mode;
+    if (!fp8bs::decode_layout(layout_code, &layout, &form, &scale_mode))
+        return FP8BS_ERR_UNSUPPORTED;
     const int g = layout == fp8bs::kDense ? 1 : num_groups;
     int cus = 0;
     fp8bs::Plan pl;
-    const int st = make_plan(layout, m, n, k, g, expected_m, INT64_MAX, &cus, &pl,
-                             fp8bs::kScaleF32, form);
+    const int st = make_plan(layout, m, n, k, g, expected_m, INT64_MAX, &cus, &pl, scale_mode,
+                             form);
     if (st != FP8BS_OK) {
         snprintf(buf, len, "%s", fp8bs_status_string(st));
         return st;
     }
-    format_plan(pl, layout, form, m, n, k, g, expected_m, cus, buf, len);
+    format_plan(pl, layout, form, m, n, k, g, expected_m, cus, buf, len, scale_mode);
     return FP8BS_OK;
 }
 

@@ -141,8 +141,9 @@ void export_plan(const Plan& p, fp8bs_plan* out);
 // K_total (0 allowed); MN-major operands need their M / N to be a multiple of 16.
 int validate_sizes(int layout, int64_t m, int n, int k, int num_groups, int form = kFormNT);
 
-// Public layout code (FP8BS_LAYOUT_*) -> internal layout and stored form; false if unknown.
-bool decode_layout(int code, int* layout, int* form);
+// Public layout code (FP8BS_LAYOUT_*, optionally OR-ed with FP8BS_LAYOUT_UE8M0) -> internal
+// layout, stored form and scale format (scale_mode may be null); false if unknown.
+bool decode_layout(int code, int* layout, int* form, int* scale_mode);
 
 // Launches instance `plan.instance` for `layout`, scale format and stored form; returns a
 // hipError_t value.

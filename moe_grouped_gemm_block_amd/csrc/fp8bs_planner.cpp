@@ -24,14 +24,17 @@ const InstanceShape kInstances[] = {
 #undef FP8BS_INSTANCE
 const int kNumInstances = (int)(sizeof(kInstances) / sizeof(kInstances[0]));
 
-bool decode_layout(int code, int* layout, int* form) {
+bool decode_layout(int code, int* layout, int* form, int* scale_mode) {
     static const int table[7][2] = {{kDense, kFormNT},     {kContiguous, kFormNT},
                                     {kMasked, kFormNT},    {kKGrouped, kFormTN},
                                     {kDense, kFormNN},     {kDense, kFormTN},
                                     {kDense, kFormTT}};
+    const bool e8 = (code & FP8BS_LAYOUT_UE8M0) != 0;
+    code &= ~FP8BS_LAYOUT_UE8M0;
     if (code < 0 || code > 6) return false;
     *layout = table[code][0];
     *form = table[code][1];
+    if (scale_mode) *scale_mode = e8 ? kScaleUE8M0 : kScaleF32;
     return true;
 }
 
@@ -301,11 +304,12 @@ extern "C" int fp8bs_plan_query(int layout_code, int64_t m, int n, int k, int nu
                                 int expected_m, int num_cus, int64_t workspace_bytes,
                                 fp8bs_plan* out) {
     if (!out) return FP8BS_ERR_POINTER;
-    int layout, form;
-    if (!fp8bs::decode_layout(layout_code, &layout, &form)) return FP8BS_ERR_UNSUPPORTED;
+    int layout, form, scale_mode;
+    if (!fp8bs::decode_layout(layout_code, &layout, &form, &scale_mode))
+        return FP8BS_ERR_UNSUPPORTED;
     fp8bs::Plan p;
     int st = fp8bs::plan_request(layout, m, n, k, layout == fp8bs::kDense ? 1 : num_groups,
-                                 expected_m, num_cus, workspace_bytes, &p, fp8bs::kScaleF32, form);
+                                 expected_m, num_cus, workspace_bytes, &p, scale_mode, form);
     if (st != FP8BS_OK) return st;
     fp8bs::export_plan(p, out);
     return FP8BS_OK;
@@ -314,7 +318,7 @@ extern "C" int fp8bs_plan_query(int layout_code, int64_t m, int n, int k, int nu
 extern "C" int64_t fp8bs_count_tiles(int layout_code, int64_t m, int n, int num_groups,
                                      int block_m, int block_n) {
     int layout, form;
-    if (!fp8bs::decode_layout(layout_code, &layout, &form)) return -1;
+    if (!fp8bs::decode_layout(layout_code, &layout, &form, nullptr)) return -1;
     if (m < 0 || n < 1 || block_m < 1 || block_n < 1) return -1;
     const bool per_group = layout == fp8bs::kMasked || layout == fp8bs::kKGrouped;
     if (per_group && num_groups < 1) return -1;

@@ -309,3 +309,58 @@ def test_ue8m0_stored_form_and_k_grouped_entry_points_validate_before_launching(
     # UE8M0 plans exist for every form and the K-grouped layout
     both = {i["instance"] for i in fp8bs.instances() if i["mn"] and i["ue8m0"]}
     assert both
+
+
+def test_test_pins_belong_to_the_calling_thread():
+    """A pin set by one thread is invisible to another thread's calls (the setters return
+    the calling thread's previous value)."""
+    import threading
+    assert fp8bs.force_instance(2) == -1
+    assert fp8bs.force_splits(5) == 0
+    seen = {}
+
+    def other():
+        seen["inst"] = fp8bs.force_instance(4)     # this thread's own pin: starts unpinned
+        seen["splits"] = fp8bs.force_splits(2)
+        seen["inst2"] = fp8bs.force_instance(-1)
+        seen["splits2"] = fp8bs.force_splits(0)
+
+    try:
+        th = threading.Thread(target=other)
+        th.start()
+        th.join()
+        assert seen == {"inst": -1, "splits": 0, "inst2": 4, "splits2": 2}
+        # the other thread's pins did not touch this thread's
+        assert fp8bs.force_instance(-1) == 2
+        assert fp8bs.force_splits(0) == 5
+    finally:
+        fp8bs.force_instance(-1)
+        fp8bs.force_splits(0)
+
+
+def test_ue8m0_layout_flag_plans_for_the_packed_scale_calls():
+    """OR-ing LAYOUT_UE8M0 into a layout code plans for the _ue8m0 call, which can only run
+    instances compiled for packed power-of-two scales; without it the plan may pick one that
+    is not (the B-streaming decode tiles)."""
+    inst = fp8bs.instances()
+    e8_ok = {i for i, s in enumerate(inst) if s["ue8m0"]}
+    assert e8_ok and len(e8_ok) < len(inst)
+    seen_difference = False
+    for fam in range(5):
+        for d in synth.workload_shapes(fam):
+            layout = {"dense": 0, "contiguous": 1, "masked": 2}[d["kind"]]
+            m = d.get("M", 0) if layout == 0 else (33152 if layout == 1 else d["max_m"])
+            args = (m, d["N"], d["K"], d.get("G", 1), d.get("expected_m", 0), 256, 1 << 40)
+            q32 = fp8bs.plan_query(layout, *args)
+            q8 = fp8bs.plan_query(layout | fp8bs.LAYOUT_UE8M0, *args)
+            assert q8["instance"] in e8_ok and q8["ue8m0"] == 1
+            seen_difference |= q32["instance"] not in e8_ok
+    assert seen_difference
+    for code in (fp8bs.LAYOUT_K_GROUPED, fp8bs.LAYOUT_DENSE_NN, fp8bs.LAYOUT_DENSE_TN,
+                 fp8bs.LAYOUT_DENSE_TT):
+        q8 = fp8bs.plan_query(code | fp8bs.LAYOUT_UE8M0, 4096, 4096, 7168, 8, 0, 256, 1 << 40)
+        assert q8["ue8m0"] == 1 and q8["mn"] == 1
+    lib = fp8bs._load()
+    assert lib.fp8bs_workspace_size(7 | fp8bs.LAYOUT_UE8M0, 64, 256, 128, 1, 0) == -ERR_UNSUPPORTED
+    assert lib.fp8bs_count_tiles(fp8bs.LAYOUT_DENSE | fp8bs.LAYOUT_UE8M0, 256, 7168, 1, 128, 128) \
+        == 112
