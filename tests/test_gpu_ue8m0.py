@@ -138,3 +138,24 @@ def test_instance_without_the_variant_is_refused():
     p = synth.make_dense(64, 256, 256, seed=2, pow2=True)
     with pytest.raises(fp8bs.FP8BSError):
         _run(p)
+
+
+def test_queries_with_the_ue8m0_flag_describe_the_launched_plan():
+    """workspace_size / describe_config with LAYOUT_UE8M0 plan exactly what the _ue8m0 call
+    runs: the decode shape below plans a B-streaming instance for FP32 scales (not compiled
+    for UE8M0), so without the flag the sized workspace and the description would be those
+    of a plan the call cannot run.  With the flag's workspace the call splits as described
+    and matches the oracle."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    m, n, k = 64, 7168, 2048
+    code = fp8bs.LAYOUT_DENSE | fp8bs.LAYOUT_UE8M0
+    q = fp8bs.plan_query(code, m, n, k, 1, 0, cus, 1 << 40)
+    assert q["ue8m0"] == 1
+    desc = fp8bs.describe_config(code, m, n, k)
+    assert f"instance {q['instance']}" in desc and f"splits {q['splits']}" in desc
+    assert " ue8m0 " in desc
+    ws_bytes = fp8bs.workspace_size(code, m, n, k)
+    assert ws_bytes == q["workspace_bytes"]
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+    _check(synth.make_dense(m, n, k, seed=590, pow2=True), "dense, flag-sized workspace",
+           workspace=ws)
