@@ -313,6 +313,28 @@ int fp8bs_k_grouped_tn_contiguous_ue8m0(const void* a, const int32_t* sfa, const
                                         int k_total, void* workspace, size_t workspace_bytes,
                                         hipStream_t stream);
 
+/*
+ * No-allocation dense call, for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.  It computes
+ * what fp8bs_dense_nt_ws computes, with the split-K workspace taken from a library-owned
+ * device array of FP8BS_NOALLOC_SCRATCH_BYTES (32 MiB) instead of from the caller: each GPU
+ * the library runs on holds one such array from its first use until the process ends.
+ * The call allocates nothing (no hipMalloc, no allocating library routine); the caller
+ * still owns and passes a, sfa, b, sfb and d (same layouts as fp8bs_dense_nt).  The planner
+ * only picks plans whose FP32 partial tiles fit the array, so every valid size is accepted;
+ * a pinned split count (fp8bs_force_splits) that would need more is refused with
+ * FP8BS_ERR_UNSUPPORTED before anything is launched.  The array keeps the last call's
+ * partials; nothing in it has to start at zero.  Every call on one GPU shares that GPU's
+ * array: two calls that may overlap on one GPU (different streams, or a graph replayed
+ * while another call runs) race on it and must be ordered by the caller.  Returns
+ * FP8BS_ERR_HIP if the array's device address cannot be obtained.
+ */
+#define FP8BS_NOALLOC_SCRATCH_BYTES (32u << 20)
+int fp8bs_dense_nt_noalloc(const void* a, const float* sfa, const void* b, const float* sfb,
+                           void* d, int m, int n, int k, hipStream_t stream);
+/* Size of that array in bytes (FP8BS_NOALLOC_SCRATCH_BYTES). */
+size_t fp8bs_noalloc_scratch_bytes(void);
+
 /* Workspace bytes the planner's preferred plan uses for a request on the current
  * device (CU cap respected; `m` as in fp8bs_plan_query).  0 means the best plan
  * splits nothing.  Passing at least this much to a _ws call lets it use that

@@ -24,7 +24,7 @@ from typing import Optional
 __all__ = [
     "fp8bs_dense_nt", "fp8bs_grouped_contiguous_nt", "fp8bs_grouped_masked_nt",
     "fp8bs_dense_nt_ws", "fp8bs_grouped_contiguous_nt_ws", "fp8bs_grouped_masked_nt_ws",
-    "dense_nt", "grouped_contiguous_nt", "grouped_masked_nt",
+    "fp8bs_dense_nt_noalloc", "noalloc_scratch_bytes", "dense_nt", "grouped_contiguous_nt", "grouped_masked_nt",
     "get_mk_alignment", "get_sfa_ld", "set_num_cus", "get_num_cus", "plan_query",
     "workspace_size", "describe_config", "count_tiles", "instances", "force_instance",
     "force_splits", "status_string", "sfa_mn_major", "library_path", "FP8BSError",
@@ -81,6 +81,9 @@ def _load():
     lib.fp8bs_grouped_masked_nt.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P]
     S = ctypes.c_size_t
     lib.fp8bs_dense_nt_ws.argtypes = [P, P, P, P, P, I, I, I, P, S, P]
+    lib.fp8bs_dense_nt_noalloc.argtypes = [P, P, P, P, P, I, I, I, P]
+    lib.fp8bs_dense_nt_noalloc.restype = I
+    lib.fp8bs_noalloc_scratch_bytes.restype = S
     lib.fp8bs_grouped_contiguous_nt_ws.argtypes = [P, P, P, P, P, P, I, I, I, I, P, S, P]
     lib.fp8bs_grouped_masked_nt_ws.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P, S, P]
     for f in ("fp8bs_dense_nt", "fp8bs_grouped_contiguous_nt", "fp8bs_grouped_masked_nt",
@@ -388,6 +391,19 @@ def fp8bs_dense_nt_ws(a, sfa, b, sfb, d, workspace=None, stream=None):
         wp, wb, _keep = _workspace(workspace, LAYOUT_DENSE, m, n, k, 1, 0, s, a.device)
         st = _load().fp8bs_dense_nt_ws(*args, m, n, k, wp, wb, _stream_handle(s, a.device))
     _check(st, "fp8bs_dense_nt_ws")
+
+
+def fp8bs_dense_nt_noalloc(a, sfa, b, sfb, d, stream=None):
+    """fp8bs_dense_nt_ws with the split-K workspace taken from the library's own per-device
+    scratch array (nothing is allocated); calls that overlap on one GPU race on it."""
+    args, m, n, k = _dense_args(a, sfa, b, sfb, d)
+    with _on_device(a):
+        st = _load().fp8bs_dense_nt_noalloc(*args, m, n, k, _stream_handle(stream, a.device))
+    _check(st, "fp8bs_dense_nt_noalloc")
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(_load().fp8bs_noalloc_scratch_bytes())
 
 
 def fp8bs_grouped_contiguous_nt(a, sfa, b, sfb, d, grouped_layout, stream=None):

@@ -8,8 +8,15 @@
 
 #include <atomic>
 #include <cstdint>
+#include <mutex>
 
 #include "fp8bs_internal.h"
+
+// The no-allocation entry point's split-K workspace: a library-owned device array, one
+// copy per GPU (each device that loads the library holds it until the process ends).  Host
+// code never uses the array's name as an address: its device address is looked up once per
+// device with hipGetSymbolAddress and kept in g_scratch_ptr.
+static __device__ __attribute__((aligned(256))) uint8_t scratch[FP8BS_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -26,6 +33,22 @@ bool print_configs() {
         return (e && e[0] && e[0] != '0') ? 1 : 0;
     }();
     return on != 0;
+}
+
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// Device address of the current device's scratch array; nullptr on error.
+void* scratch_ptr() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::call_once(g_scratch_once[dev], [dev] {
+        void* p = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+    });
+    return g_scratch_ptr[dev];
 }
 
 // Compute units of the current device, capped by fp8bs_set_num_cus; 0 on error.
@@ -359,6 +382,21 @@ int fp8bs_k_grouped_tn_contiguous_ue8m0(const void* a, const int32_t* sfa, const
                num_groups, 0, workspace, workspace ? workspace_bytes : 0, stream,
                fp8bs::kScaleUE8M0, c, c != nullptr);
 }
+
+int fp8bs_dense_nt_noalloc(const void* a, const float* sfa, const void* b, const float* sfb,
+                           void* d, int m, int n, int k, hipStream_t stream) {
+    // sizes first: an invalid or empty request is answered without touching the device
+    const int st = fp8bs::validate_sizes(fp8bs::kDense, m, n, k, 1);
+    if (st != FP8BS_OK || m == 0) return st;
+    void* ws = scratch_ptr();
+    if (!ws) return FP8BS_ERR_HIP;
+    // The planner only picks plans whose partial tiles fit the array; a pinned split count
+    // that needs more is refused (FP8BS_ERR_UNSUPPORTED) before anything is launched.
+    return run(fp8bs::kDense, a, sfa, b, sfb, d, nullptr, m, n, k, 1, 0, ws,
+               FP8BS_NOALLOC_SCRATCH_BYTES, stream);
+}
+
+size_t fp8bs_noalloc_scratch_bytes(void) { return FP8BS_NOALLOC_SCRATCH_BYTES; }
 
 int64_t fp8bs_workspace_size(int layout_code, int64_t m, int n, int k, int num_groups,
                              int expected_m) {
