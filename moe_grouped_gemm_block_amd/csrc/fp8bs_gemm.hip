@@ -142,24 +142,11 @@ struct Tile {
     int g, m0, n0, row_limit;
 };
 
-// Schedule position -> tile.  Masked and K-grouped: group-major.  Within a slot, groups of
-// `raster` m-blocks sweep the n-blocks column by column.  Returns false when
-// the tile holds no valid row (masked: beyond masked_m; contiguous: padding).
+// Tile (slot / group g, m-block mb, n-block nb) -> its rows, columns and expert.  Returns
+// false when the tile holds no valid row (masked: beyond masked_m; contiguous: padding).
 template <int BM, int BN, int LAYOUT>
-__device__ __forceinline__ bool tile_at(const GemmParams& p, int t, Tile& tl, int pass = 0) {
-    int rest = t, g = 0;
-    if (LAYOUT == kMasked || LAYOUT == kKGrouped) {
-        const int per_slot = p.m_blocks * p.n_blocks;
-        g = t / per_slot;
-        rest = t - g * per_slot;
-    }
-    const int per_group = p.raster * p.n_blocks;
-    const int grp = rest / per_group;
-    const int r = rest - grp * per_group;
-    const int first = grp * p.raster;
-    const int rows_in = min(p.raster, p.m_blocks - first);
-    const int mb = first + r % rows_in;
-    const int nb = r / rows_in;
+__device__ __forceinline__ bool tile_at_block(const GemmParams& p, int g, int mb, int nb,
+                                              Tile& tl, int pass = 0) {
     tl.m0 = mb * BM;
     tl.n0 = nb * BN;
     tl.row_limit = p.m;
@@ -197,6 +184,25 @@ __device__ __forceinline__ bool tile_at(const GemmParams& p, int t, Tile& tl, in
     return true;
 }
 
+// Schedule position -> tile.  Masked and K-grouped: group-major.  Within a slot, groups of
+// `raster` m-blocks sweep the n-blocks column by column.  Returns false when
+// the tile holds no valid row (masked: beyond masked_m; contiguous: padding).
+template <int BM, int BN, int LAYOUT>
+__device__ __forceinline__ bool tile_at(const GemmParams& p, int t, Tile& tl, int pass = 0) {
+    int rest = t, g = 0;
+    if (LAYOUT == kMasked || LAYOUT == kKGrouped) {
+        const int per_slot = p.m_blocks * p.n_blocks;
+        g = t / per_slot;
+        rest = t - g * per_slot;
+    }
+    const int per_group = p.raster * p.n_blocks;
+    const int grp = rest / per_group;
+    const int r = rest - grp * per_group;
+    const int first = grp * p.raster;
+    const int rows_in = min(p.raster, p.m_blocks - first);
+    return tile_at_block<BM, BN, LAYOUT>(p, g, first + r % rows_in, r / rows_in, tl, pass);
+}
+
 // A work unit: K split s of tile t, chunks [c0, c1).
 struct Unit {
     int u, t, s, c0, c1;
@@ -207,16 +213,97 @@ struct NoEmptyUnits {
     __device__ void operator()(const Unit&) const {}
 };
 
+// Contiguous layout with 256-row tiles: the work list of (m-block, pass) pairs, one pass per
+// expert an m-block holds (two when its 128-row halves belong to different experts),
+// numbered densely so that the persistent workgroups share the real work evenly (unit
+// indices past the list are empty and end the workgroup's stream).  "Virtual m-block" v
+// is m-block mb's pass q, v = mb + (two-expert m-blocks before mb) + q; the i-th
+// two-expert m-block B_i (in order) therefore has its second pass at v = B_i + i + 1.
+// Experts are contiguous segments, so at most G - 1 m-blocks hold two; the list keeps up to
+// 64 of them, lane i of one register holding B_i + i + 1 (lanes past the count: INT_MAX),
+// and is decoded with two ballots -- no memory access inside the chunk loop.
+constexpr int kPassListMax = 64;
+struct PassList {
+    int count;             // two-expert m-blocks; < 0: list not built, sparse pass-major units
+    int vblocks;           // m-blocks plus two-expert m-blocks
+    int second;            // this lane's B_i + i + 1
+};
+
+// Virtual m-block v -> (m-block, pass).
+__device__ __forceinline__ void pass_decode(const PassList& pl, int v, int& mb, int& pass) {
+    const int before = __popcll(__ballot(pl.second < v));   // second passes before v
+    pass = __ballot(pl.second == v) != 0ull ? 1 : 0;
+    mb = v - before - pass;
+}
+
+// Builds the list for this workgroup's wavefront (every wavefront builds its own copy from
+// grouped_layout; no LDS).  Returns count = -1 when more than kPassListMax m-blocks hold two
+// experts.
+template <int BM>
+__device__ __forceinline__ PassList pass_list_build(const GemmParams& p, int lane) {
+    PassList pl{0, p.m_blocks, 0x7fffffff};
+    int count = 0;
+    for (int w0 = 0; w0 < p.m_blocks; w0 += 64) {
+        const int mb = w0 + lane;
+        bool two = false;
+        if (mb < p.m_blocks) {
+            const int r0 = mb * BM, r1 = r0 + 128;
+            const int e0 = p.grouped_layout[r0];
+            const int e1 = r1 < p.m ? p.grouped_layout[r1] : -1;
+            two = e0 >= 0 && e0 < p.num_groups && e1 >= 0 && e1 < p.num_groups && e0 != e1;
+        }
+        const uint64_t bits = __ballot(two);
+        const int n = __popcll(bits);
+        if (count + n > kPassListMax) return PassList{-1, p.m_blocks, 0x7fffffff};
+        // lane count + k takes the k-th set bit of this word
+        const int k = lane - count;
+        if (k >= 0 && k < n) {
+            int pos = 0;
+            for (int step = 32; step > 0; step >>= 1)
+                if (__popcll(bits & ((1ull << (pos + step)) - 1ull)) <= k) pos += step;
+            pl.second = (w0 + pos) + lane + 1;
+        }
+        count += n;
+    }
+    pl.count = count;
+    pl.vblocks = p.m_blocks + count;
+    return pl;
+}
+
 // The next unit at or after schedule position u (stepping by the grid) that has chunks to
 // multiply.  K-grouped: a unit's chunks are split s of its group's chunks, and a unit
 // with none (an empty group, or more splits than the group has chunks) is handed to
 // on_empty -- which stores its all-zero result -- and skipped.
 template <int BM, int BN, int LAYOUT, typename OnEmpty = NoEmptyUnits>
 __device__ __forceinline__ bool next_unit(const GemmParams& p, int u, Unit& w,
-                                          OnEmpty&& on_empty = OnEmpty{}) {
+                                          OnEmpty&& on_empty = OnEmpty{},
+                                          const PassList* pl = nullptr) {
     const int kchunks = p.k / 128;
-    // contiguous layout, 256-row tiles: units are (pass, tile), pass-major, never split
+    // contiguous layout, 256-row tiles: units are (pass, tile), never split
     constexpr bool PASSES = LAYOUT == kContiguous && BM > 128;
+    if constexpr (PASSES) {
+        if (pl && pl->count >= 0) {
+            // dense (m-block, pass) list, rastered like tile_at's m-blocks
+            for (; u < pl->vblocks * p.n_blocks; u += gridDim.x) {
+                const int per_group = p.raster * p.n_blocks;
+                const int grp = u / per_group;
+                const int r = u - grp * per_group;
+                const int first = grp * p.raster;
+                const int rows_in = min(p.raster, pl->vblocks - first);
+                int mb, pass;
+                pass_decode(*pl, first + r % rows_in, mb, pass);
+                const int nb = r / rows_in;
+                if (!tile_at_block<BM, BN, LAYOUT>(p, 0, mb, nb, w.tl, pass)) continue;
+                w.u = u;
+                w.t = mb * p.n_blocks + nb;
+                w.s = 0;
+                w.c0 = 0;
+                w.c1 = kchunks;
+                return true;
+            }
+            return false;
+        }
+    }
     for (; u < p.units; u += gridDim.x) {
         const int q = u / p.tiles, t = u - q * p.tiles;
         const int s = PASSES ? 0 : q;
@@ -727,9 +814,15 @@ __global__ void __launch_bounds__(64 * WM * WN) fp8bs_gemm_kernel(GemmParams p) 
         }
     };
 
+    // ---- contiguous layout, 256-row tiles: the dense (m-block, pass) work list ----
+    constexpr bool PASSES = LAYOUT == kContiguous && BM > 128;
+    PassList plist{-1, 0, 0};
+    if constexpr (PASSES) plist = pass_list_build<BM>(p, lane);
+    const PassList* pl = PASSES ? &plist : nullptr;
+
     // ---- the two cursors over this workgroup's (unit, chunk) stream ----
     Unit cur;                                          // the chunk being multiplied
-    if (!next_unit<BM, BN, LAYOUT>(p, logical_block_id(), cur, on_empty)) return;
+    if (!next_unit<BM, BN, LAYOUT>(p, logical_block_id(), cur, on_empty, pl)) return;
     Unit isu = cur;                                    // the next chunk to copy
     int ic = cur.c0;
     bool live = true;                                  // false: stream exhausted, repeat last
@@ -737,7 +830,7 @@ __global__ void __launch_bounds__(64 * WM * WN) fp8bs_gemm_kernel(GemmParams p) 
         if (!live) return;
         if (++ic < isu.c1) return;
         Unit nx;
-        if (next_unit<BM, BN, LAYOUT>(p, isu.u + gridDim.x, nx)) {
+        if (next_unit<BM, BN, LAYOUT>(p, isu.u + gridDim.x, nx, NoEmptyUnits{}, pl)) {
             isu = nx;
             ic = nx.c0;
         } else {
@@ -914,7 +1007,7 @@ __global__ void __launch_bounds__(64 * WM * WN) fp8bs_gemm_kernel(GemmParams p) 
             for (int i = 0; i < TM; ++i)
 #pragma unroll
                 for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (!next_unit<BM, BN, LAYOUT>(p, cur.u + gridDim.x, cur, on_empty)) break;
+            if (!next_unit<BM, BN, LAYOUT>(p, cur.u + gridDim.x, cur, on_empty, pl)) break;
             c = cur.c0;
         } else {
             ++c;

@@ -83,6 +83,25 @@ def test_contiguous_planner_multinomial():
     _run_and_check(p, "contiguous multinomial")
 
 
+_TWO_PASS = [i["instance"] for i in fp8bs.instances() if i["block_m"] == 256]
+
+
+@pytest.mark.parametrize("inst", _TWO_PASS)
+@pytest.mark.parametrize("experts", [40, 200])
+def test_contiguous_many_two_expert_tiles(inst, experts):
+    """256-row tiles over many experts whose segments start at odd 128-row blocks, so that
+    many m-blocks hold two experts: with 40 experts 14 do, within the schedule's dense list
+    of two-expert m-blocks (at most 64); with 200 experts 75 do, past it (the sparse,
+    pass-major order); empty experts and one-row segments included."""
+    rng = np.random.default_rng(7000 + experts)
+    sizes = [0, 1, 100, 128, 129, 300] if experts == 40 else [0, 1, 100, 129, 300]
+    counts = [int(c) for c in rng.choice(sizes, size=experts)]
+    counts[experts // 2] = 128 * 3 + 5
+    fp8bs.force_instance(inst)
+    p = synth.make_contiguous(experts, 136, 256, seed=7100 + experts, counts=counts)
+    _run_and_check(p, f"contiguous {experts} experts inst {inst}", workspace=False)
+
+
 @pytest.mark.parametrize("inst", range(N_INST))
 def test_masked_every_instance(inst):
     fp8bs.force_instance(inst)
