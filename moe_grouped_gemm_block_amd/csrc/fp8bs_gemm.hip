@@ -1072,7 +1072,30 @@ __global__ void __launch_bounds__(64 * NW) fp8bs_stream_kernel(GemmParams p) {
     static_assert((PD - 1) * OPC <= 63, "vmcnt range");
     constexpr bool UNIFORM_SB = (128 % WTN == 0) && (BN % 128 == 0 || 128 % BN == 0);
 
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
+    // One LDS array per ring stage.  The compiler places its own waits before LDS reads
+    // by which LDS variable they touch: with a single ring array, every read of chunk c
+    // would wait for the copies of chunks c+1 .. c+NS-1 too (all in flight), which takes
+    // the ring's depth away.  Stage indices are compile-time constants after unrolling.
+    static_assert(NS <= 10, "ring stages");
+    constexpr int S2 = NS > 2 ? STAGE : 1, S3 = NS > 3 ? STAGE : 1, S4 = NS > 4 ? STAGE : 1;
+    constexpr int S5 = NS > 5 ? STAGE : 1, S6 = NS > 6 ? STAGE : 1, S7 = NS > 7 ? STAGE : 1;
+    constexpr int S8 = NS > 8 ? STAGE : 1, S9 = NS > 9 ? STAGE : 1;
+    __shared__ __attribute__((aligned(256))) uint8_t ring0[STAGE], ring1[STAGE], ring2[S2],
+        ring3[S3], ring4[S4], ring5[S5], ring6[S6], ring7[S7], ring8[S8], ring9[S9];
+    auto stage_at = [&](int s) -> uint8_t* {
+        switch (s) {
+            case 0: return ring0;
+            case 1: return ring1;
+            case 2: return ring2;
+            case 3: return ring3;
+            case 4: return ring4;
+            case 5: return ring5;
+            case 6: return ring6;
+            case 7: return ring7;
+            case 8: return ring8;
+            default: return ring9;
+        }
+    };
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1131,7 +1154,7 @@ __global__ void __launch_bounds__(64 * NW) fp8bs_stream_kernel(GemmParams p) {
     // ---- A / scale copies of chunk c into stage s ----
     const int cp_row = lane >> 3, cp_slot = lane & 7;
     auto issue_a = [&](int c, int s) {
-        uint8_t* st = smem + s * STAGE;
+        uint8_t* st = stage_at(s);
         const uint8_t* a_base = p.a + (LAYOUT == kMasked ? (int64_t)tl.g * p.m * K : (int64_t)0) +
                                 (int64_t)c * 128;
 #pragma unroll
@@ -1177,7 +1200,7 @@ __global__ void __launch_bounds__(64 * NW) fp8bs_stream_kernel(GemmParams p) {
 
     // multiply chunk in stage / ring slot `slot`
     auto compute = [&](int slot, const i32x8 (&bf)[TN]) {
-        const uint8_t* st = smem + slot * STAGE;
+        const uint8_t* st = stage_at(slot);
         float sa[TM];
         {
             const float* sap = (const float*)(st + sa_rd);

@@ -206,6 +206,21 @@ def test_split_k_reuses_a_caller_workspace():
         check_full(p, dp.result(), oracle_full(p), "caller workspace")
 
 
+def test_split_k_workspace_shared_by_calls_of_other_shapes():
+    """Split calls of different tile counts and split counts in turn on one workspace
+    that starts as garbage: each call's per-tile arrival words overlap what the others
+    left there (partials or words), and every result still matches the oracle."""
+    ws = torch.randint(0, 256, (64 * 1024 * 1024,), dtype=torch.uint8, device="cuda")
+    cases = [(128, 2112, 7168, 7), (64, 512, 1024, 4), (200, 300, 640, 5), (128, 2112, 7168, 7)]
+    for n, (m, nn, k, splits) in enumerate(cases):
+        _say(f"shared workspace call {n}: {m}x{nn}x{k} splits {splits}")
+        p = synth.make_dense(m, nn, k, seed=117 + n)
+        dp = DeviceProblem(p)
+        fp8bs.force_splits(splits)
+        fp8bs.fp8bs_dense_nt_ws(dp.a, dp.sfa, dp.b, dp.sfb, dp.d, workspace=ws)
+        check_full(p, dp.result(), oracle_full(p), f"shared workspace call {n}")
+
+
 def test_split_k_short_workspace_is_refused_when_pinned():
     p = synth.make_dense(64, 512, 1024, seed=116)
     dp = DeviceProblem(p)
