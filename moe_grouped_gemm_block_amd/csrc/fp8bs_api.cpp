@@ -131,8 +131,10 @@ int make_plan(int layout, int64_t m, int n, int k, int num_groups, int expected_
             return FP8BS_OK;
         }
     }
+    // a pinned split count alone: the best instance that runs with it (so that the plan a
+    // workspace was sized for is found again when that workspace is lent)
     int st = fp8bs::plan_request(layout, m, n, k, num_groups, expected_m, cus, ws_bytes, pl,
-                                 scale_mode, form);
+                                 scale_mode, form, forced >= 0 ? 0 : splits);
     if (st != FP8BS_OK) return st;
     if (forced >= 0 || splits > 0)
         st = fp8bs::plan_instance(forced >= 0 ? forced : pl->instance, splits, layout, m, n, k,

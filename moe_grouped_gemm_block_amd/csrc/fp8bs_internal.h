@@ -122,11 +122,12 @@ constexpr int passes_per_tile(int layout, int block_m) {
 int64_t split_workspace_bytes(const InstanceShape& shape, int64_t tiles, int splits);
 
 // Host planner: deterministic choice of an instance, a K split count (only when the
-// caller offers at least that much workspace) and launch shape.
+// caller offers at least that much workspace) and launch shape; splits > 0 restricts the
+// choice to instances that run with that split count.
 // Returns FP8BS_OK or an error status.  No device access.
 int plan_request(int layout, int64_t m, int n, int k, int num_groups, int expected_m,
                  int num_cus, int64_t workspace_bytes, Plan* out, int scale_mode = kScaleF32,
-                 int form = kFormNT);
+                 int form = kFormNT, int splits = 0);
 
 // Launch shape for a given instance and split count (used when either is pinned;
 // splits < 1 picks the best split count for the instance within the workspace).

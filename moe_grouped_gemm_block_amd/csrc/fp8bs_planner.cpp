@@ -81,11 +81,17 @@ int64_t split_workspace_bytes(const InstanceShape& shape, int64_t tiles, int spl
 // written once and read once); a split launch adds the reduction kernel; and a launch
 // that leaves CUs idle keeps fewer loads in flight, so under-fill is penalised.
 static const double kHbmBytesPerNs = 8.0e12 / 1.0e9;
-static const double kReduceFixedNs = 4300.0;         // second launch: 4.2-4.8 us traced
-static const double kReduceBytesPerNs = 4.0e12 / 1.0e9;
+// second launch: fitted to traced cold decode calls (3.2 us + bytes / 9 TB/s), with the
+// fixed part raised to cover the gap between the two dispatches
+static const double kReduceFixedNs = 5000.0;
+static const double kReduceBytesPerNs = 9.0e12 / 1.0e9;
 static const int kMaxSplits = 16;
 static const double kRidgeFlopPerByte = 629.0;       // dense FP8 MFMA peak / HBM bandwidth
-static const double kStagedStreamingBias = 1.25;
+// dense: measured on the M=128 and decode shapes, where the B-streaming tiles won every
+// comparison; grouped layouts: the masked MoE shapes, where the 256x256 staged tile (B read
+// once per slot) beats every B-streaming tile by 1.6x
+static const double kStagedStreamingBias = 2.0;
+static const double kStagedStreamingBiasGrouped = 1.25;
 
 namespace {
 
@@ -181,7 +187,8 @@ double estimate(const Request& r, const InstanceShape& s, int splits) {
     // The staged kernels' streaming-regime fit is loose (their direct-to-LDS copies slow
     // down unevenly as they miss in L2); measured, they lose to the B-streaming kernel
     // unless the model favours them by a wide margin.
-    if (streaming && s.kind == kStaged) t *= kStagedStreamingBias;
+    if (streaming && s.kind == kStaged)
+        t *= r.layout == kDense ? kStagedStreamingBias : kStagedStreamingBiasGrouped;
     if (kg)                                      // measured K-grouped cost of the instance
         t *= (r.scale_mode == kScaleUE8M0 ? s.mn_e8 : s.mn) / 100.0;
     const double d_bytes = (double)r.G * r.eff_rows * r.n * (kg ? 4 : 2);
@@ -250,7 +257,8 @@ int plan_instance(int instance, int splits, int layout, int64_t m, int n, int k,
 }
 
 int plan_request(int layout, int64_t m, int n, int k, int num_groups, int expected_m,
-                 int num_cus, int64_t workspace_bytes, Plan* out, int scale_mode, int form) {
+                 int num_cus, int64_t workspace_bytes, Plan* out, int scale_mode, int form,
+                 int splits) {
     int st = validate_sizes(layout, m, n, k, layout == kDense ? 1 : num_groups, form);
     if (st != FP8BS_OK) return st;
     if (num_cus < 1) return FP8BS_ERR_UNSUPPORTED;
@@ -262,7 +270,7 @@ int plan_request(int layout, int64_t m, int n, int k, int num_groups, int expect
         const InstanceShape& s = kInstances[i];
         if (!instance_fits(r, s)) continue;
         if (scale_mode == kScaleUE8M0 && !s.ue8m0) continue;
-        for (int sp = 1; sp <= kMaxSplits; ++sp) {
+        for (int sp = splits > 0 ? splits : 1; sp <= (splits > 0 ? splits : kMaxSplits); ++sp) {
             const double t = estimate(r, s, sp);
             if (t < 0) continue;
             if (best < 0 || t < best_t * (1.0 - 1e-9)) {
