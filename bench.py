@@ -63,10 +63,10 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def load_traffic(name: str):
-    """HBM bytes per launch measured with rocprofv3 --pmc (FETCH_SIZE + WRITE_SIZE, scaled
-    by a plain copy kernel) for this kernel source; None when absent or stale."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+def _profile_entry(fname: str, name: str):
+    """The record for shape `name` in profiles/<fname>, when it was taken on this kernel
+    source; None when absent, unreadable or stale."""
+    path = os.path.join(ROOT, "profiles", fname)
     if not os.path.exists(path):
         return None
     try:
@@ -75,8 +75,24 @@ def load_traffic(name: str):
         return None
     if data.get("source_sha256") != kernel_source_hash():
         return None
-    entry = data.get("shapes", {}).get(name)
+    return data.get("shapes", {}).get(name)
+
+
+def load_traffic(name: str):
+    """HBM bytes per launch measured with rocprofv3 --pmc (FETCH_SIZE + WRITE_SIZE, scaled
+    by a plain copy kernel) for this kernel source; None when absent or stale."""
+    entry = _profile_entry("traffic.json", name)
     return None if entry is None else entry.get("bytes_per_launch")
+
+
+def load_mfma_busy(name: str):
+    """MFMA busy fraction and shader clock of the kernel from rocprofv3 --pmc
+    (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE) for this kernel source; None when
+    absent or stale."""
+    entry = _profile_entry("mfma.json", name)
+    if entry is None:
+        return None
+    return {"busy_frac": entry.get("mfma_busy_frac"), "sclk_ghz": entry.get("sclk_ghz")}
 
 
 def cpu_model() -> str:
@@ -301,6 +317,7 @@ def roofline_of(d):
         roof = {"bound": "hbm", "achieved": d["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": d["gbs"] / PEAK_HBM_GBS}
     roof["traffic"] = load_traffic(d["name"])
+    roof["mfma_busy"] = load_mfma_busy(d["name"])
     roof["kernel"] = d["name"]
     roof["algorithmic_per_launch"] = {"gflop": d["gflop"], "mbytes": d["mbytes"]}
     roof["avg_launch_us"] = d["avg_us"]

@@ -217,6 +217,13 @@ __device__ __forceinline__ bool tile_at(const GemmParams& p, int t, Tile& tl, in
     return tile_at_block<BM, BN, LAYOUT>(p, g, first + r % rows_in, r / rows_in, tl, pass);
 }
 
+// First chunk of K split s of n chunks in `splits` ranges: floor(s * n / splits), in 32-bit
+// unsigned arithmetic (the planner keeps splits * n below 2^32; a 64-bit division would cost
+// every workgroup a division loop in its prologue).
+__device__ __forceinline__ int split_bound(int s, int n, int splits) {
+    return (int)((uint32_t)s * (uint32_t)n / (uint32_t)splits);
+}
+
 // A work unit: K split s of tile t, chunks [c0, c1).
 struct Unit {
     int u, t, s, c0, c1;
@@ -328,15 +335,15 @@ __device__ __forceinline__ bool next_unit(const GemmParams& p, int u, Unit& w,
         if constexpr (LAYOUT == kKGrouped) {
             const int cb = p.kg_chunk0[w.tl.g];
             const int nch = p.kg_chunk0[w.tl.g + 1] - cb;
-            w.c0 = cb + (int)((int64_t)s * nch / p.splits);
-            w.c1 = cb + (int)((int64_t)(s + 1) * nch / p.splits);
+            w.c0 = cb + split_bound(s, nch, p.splits);
+            w.c1 = cb + split_bound(s + 1, nch, p.splits);
             if (w.c0 == w.c1) {
                 on_empty(w);
                 continue;
             }
         } else {
-            w.c0 = (int)((int64_t)s * kchunks / p.splits);
-            w.c1 = (int)((int64_t)(s + 1) * kchunks / p.splits);
+            w.c0 = split_bound(s, kchunks, p.splits);
+            w.c1 = split_bound(s + 1, kchunks, p.splits);
         }
         return true;
     }

@@ -156,6 +156,8 @@ double estimate(const Request& r, const InstanceShape& s, int splits) {
     // group's chunks are empty units -- but the estimate uses the mean group)
     const int max_splits = kg ? (r.k / 128 > 1 ? r.k / 128 : 1) : kchunks;
     if (splits < 1 || splits > max_splits) return -1.0;
+    // the kernels compute split bounds as splits x chunks in 32 bits
+    if ((int64_t)splits * (r.k / 128) >= ((int64_t)1 << 32)) return -1.0;
     // two-pass contiguous tiles are never split
     const int passes = passes_per_tile(r.layout, s.block_m);
     if (passes > 1 && splits > 1) return -1.0;

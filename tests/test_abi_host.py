@@ -59,6 +59,14 @@ def test_page_tile_count_example():
     assert p["tiles"] >= 112
 
 
+def test_planner_reads_b_once_for_the_m128_decode_shape():
+    # M=128, N=2112, K=7168 with a workspace: a B-streaming tile covering all 128 rows, so
+    # that every weight byte is read once, split along K to occupy the CUs
+    p = fp8bs.plan_query(fp8bs.LAYOUT_DENSE, 128, 2112, 7168, num_cus=256, workspace_bytes=1 << 30)
+    assert p["kind"] == 1 and p["block_m"] >= 128
+    assert p["splits"] > 1 and p["tiles"] * p["splits"] >= 0.75 * 256
+
+
 def test_planner_fills_the_cus_for_the_decode_tile_case():
     # M=256, N=7168: 128x128 tiles would leave more than half of the 256 CUs idle
     p = fp8bs.plan_query(fp8bs.LAYOUT_DENSE, 256, 7168, 7168, num_cus=256)

@@ -107,3 +107,16 @@ def test_input_hash_covers_group_data():
     p.layout = p.layout.copy()
     p.layout[0] = -1
     assert bench.input_sha256(p) != h
+
+
+def test_mfma_busy_reported_only_for_the_source_it_was_taken_on(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    _fake_tree(tmp_path, "kernel v1")
+    h1 = bench.kernel_source_hash()
+    entry = {"mfma_busy_frac": 0.42, "sclk_ghz": 2.05}
+    (tmp_path / "profiles" / "mfma.json").write_text(
+        json.dumps({"source_sha256": h1, "shapes": {"shape_a": entry}}))
+    assert bench.load_mfma_busy("shape_a") == {"busy_frac": 0.42, "sclk_ghz": 2.05}
+    assert bench.load_mfma_busy("shape_b") is None
+    _fake_tree(tmp_path, "kernel v2")
+    assert bench.load_mfma_busy("shape_a") is None

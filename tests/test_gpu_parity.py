@@ -221,6 +221,22 @@ def test_split_k_workspace_shared_by_calls_of_other_shapes():
         check_full(p, dp.result(), oracle_full(p), f"shared workspace call {n}")
 
 
+@pytest.mark.parametrize("splits", [2, 3, 5, 7])
+def test_pinned_split_runs_in_the_workspace_it_was_sized_for(splits):
+    """With only the split count pinned, fp8bs_workspace_size and the call must agree on
+    the plan: a workspace of exactly the reported size is accepted."""
+    for n, (m, nn, k) in enumerate([(20, 30, 896), (128, 2112, 7168), (64, 4096, 1024),
+                                    (256, 700, 2048)]):
+        fp8bs.force_splits(splits)
+        wsz = fp8bs.workspace_size(fp8bs.LAYOUT_DENSE, m, nn, k)
+        _say(f"pinned splits {splits}: {m}x{nn}x{k} workspace {wsz}")
+        p = synth.make_dense(m, nn, k, seed=130 + 10 * splits + n)
+        dp = DeviceProblem(p)
+        ws = torch.empty(max(wsz, 16), dtype=torch.uint8, device="cuda")
+        fp8bs.fp8bs_dense_nt_ws(dp.a, dp.sfa, dp.b, dp.sfb, dp.d, workspace=ws)
+        check_full(p, dp.result(), oracle_full(p), f"pinned splits {splits} {m}x{nn}x{k}")
+
+
 def test_split_k_short_workspace_is_refused_when_pinned():
     p = synth.make_dense(64, 512, 1024, seed=116)
     dp = DeviceProblem(p)
