@@ -409,8 +409,10 @@ int fp8bs_get_num_cus(void);
 int fp8bs_force_instance(int i);
 
 /* Pins the K split count of the calling thread's later _ws calls to s >= 1 (1 = no
- * split); 0 restores the planner's choice.  A pinned count that the request cannot use
- * (s > K/128, or more workspace than lent) makes the call fail with
+ * split); 0 restores the planner's choice.  Without a pinned instance the planner then
+ * picks the best instance that runs with s splits (fp8bs_workspace_size reports that
+ * plan's workspace).  A pinned count that the request cannot use (s > K/128, s x K/128
+ * of 2^32 or more, or more workspace than lent) makes the call fail with
  * FP8BS_ERR_UNSUPPORTED.  For testing and measuring; changes speed, and
  * results only within the bound stated for the _ws calls.  Returns the previous
  * setting, or -1 for s < 0. */
