@@ -51,7 +51,7 @@ FAMILY_NAMES = {
 DEFAULT_FAMILY = 3
 DEFAULT_OTHERS = "0,1,2,4"
 OTHER_STEPS = 10                  # timed steps of each non-headline family (at most --steps)
-CPU_SAMPLE_GFLOP = 700.0          # oracle work of the CPU baseline (about 10 s on 16 cores)
+CPU_SAMPLE_GFLOP = 1000.0         # oracle work of the CPU baseline (about 13 s on 16 cores)
 COPY_PROBE_BYTES = 512 << 20
 
 

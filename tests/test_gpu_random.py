@@ -5,6 +5,8 @@ against the oracle over the whole output (valid rows to tolerance, the rest unto
 and the same for the K-grouped weight-gradient call (group sizes with empty groups, FP32
 addend in place or apart, UE8M0 scales, split K).  Every case is fixed by the seed, so a
 failure names a reproducible case."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -19,8 +21,9 @@ import test_gpu_ue8m0 as ue8m0_t
 
 pytestmark = pytest.mark.gpu
 
-SEED = 20261203
-N_CASES = 160
+# FP8BS_RANDOM_SEED / FP8BS_RANDOM_CASES draw another (or a longer) series of cases
+SEED = int(os.environ.get("FP8BS_RANDOM_SEED", "20261203"))
+N_CASES = int(os.environ.get("FP8BS_RANDOM_CASES", "160"))
 INSTANCES = fp8bs.instances()
 VARIANTS = ["ws", "ws", "nows", "addend", "ue8m0", "form"]
 
@@ -92,7 +95,7 @@ def test_random_case(i):
         check_full(p, dp.result(), oracle_full(p), what)
 
 
-N_KG_CASES = 40
+N_KG_CASES = int(os.environ.get("FP8BS_RANDOM_KG_CASES", "40"))
 
 
 def _kg_case(i):
