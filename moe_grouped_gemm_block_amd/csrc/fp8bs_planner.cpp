@@ -177,12 +177,17 @@ double estimate(const Request& r, const InstanceShape& s, int splits) {
     // a second pass runs only for a tile whose two blocks hold different experts: about
     // one tile in 32 for segments of thousands of rows
     const int64_t units = passes > 1 ? tiles + (tiles + 31) / 32 : tiles * splits;
-    const int64_t per_cu = (units + r.num_cus - 1) / r.num_cus;
+    int64_t per_cu = (units + r.num_cus - 1) / r.num_cus;
     const int64_t chunks_per_unit = (kchunks + splits - 1) / splits;
     // Operands stream from HBM when a byte of A or B feeds fewer flops than the chip's
     // ridge point (MFMA peak / HBM bandwidth): 2 x rows x N / (rows + N) flops per byte.
     const bool streaming =
         2.0 * (double)r.eff_rows * r.n / ((double)r.eff_rows + r.n) < kRidgeFlopPerByte;
+    // The compute-regime chunk cost is the CU's throughput with wg_per_cu workgroups
+    // sharing it; a workgroup alone on its CU (fewer units than CUs) is not faster per
+    // chunk than that (measured on MI355X: the 128x128 two-workgroup tile takes 1.37-1.41 us
+    // per chunk alone, twice its shared-CU cost).
+    if (!streaming && per_cu < s.wg_per_cu) per_cu = s.wg_per_cu;
     const double c_ns = streaming ? s.stream_chunk_ns : s.chunk_ns;
     const double t_ns = streaming ? s.stream_tile_ns : s.tile_ns;
     double t = per_cu * (chunks_per_unit * c_ns + t_ns);

@@ -67,6 +67,15 @@ def test_planner_reads_b_once_for_the_m128_decode_shape():
     assert p["splits"] > 1 and p["tiles"] * p["splits"] >= 0.75 * 256
 
 
+def test_planner_does_not_count_a_lone_workgroup_at_its_shared_cu_rate():
+    # M=512, N=7168, K=7168: unsplit 128x128 tiles (two workgroups per CU when the grid
+    # fills every slot) give 224 units, one workgroup per CU; alone, such a workgroup takes
+    # about twice the shared-CU chunk cost (78 us traced cold on MI355X, against 59 us for
+    # 256x256 tiles split four ways), so that plan must not be chosen
+    p = fp8bs.plan_query(fp8bs.LAYOUT_DENSE, 512, 7168, 7168, num_cus=256, workspace_bytes=1 << 30)
+    assert not (p["wg_per_cu"] > 1 and p["tiles"] * p["splits"] <= 256)
+
+
 def test_planner_fills_the_cus_for_the_decode_tile_case():
     # M=256, N=7168: 128x128 tiles would leave more than half of the 256 CUs idle
     p = fp8bs.plan_query(fp8bs.LAYOUT_DENSE, 256, 7168, 7168, num_cus=256)
